@@ -1,0 +1,307 @@
+/*
+ * moonep_oracle.c -- plain, slow, obviously correct CPU oracle for the balanced
+ * expert-parallel plan and the four data moves it drives.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The product path (the HIP
+ * library under token_dispatch_amd/) shares no code with it and never calls it.
+ *
+ * What is computed, and where it is stated (MoonEP write-ups):
+ *   - the skew metric maxvio = max_e(T_e / Tbar) - 1, T_e = assignments routed to
+ *     expert e, Tbar = the count under perfect balance
+ *     (news.hamidun.com EN, "Why expert parallelism is needed";
+ *      blog.schoergendorfer.com, "The problem MoonEP targets");
+ *   - every rank receives exactly S x K assignments whatever the skew, reached by
+ *     scheduling a few duplicate experts online from the current router output;
+ *     duplicates are fetched before compute and their gradients are reduced back
+ *     to the home ranks (news.hamidun.com EN, "How MoonEP works");
+ *   - tokens are written straight into static buffers at positions grouped by
+ *     expert (news.hamidun.com EN, "Why this matters to engineers").
+ * The pages give no algorithm beyond this. The concrete plan below is the plain
+ * water-fill reading: contiguous home experts (e / (E/R)), keep the first
+ * min(L_r, S*K) home assignments of each rank in (expert, token, k) order, send
+ * the rest -- ordered by (home rank, expert, token, k) -- to the deficit slots of
+ * the ranks in rank order; every maximal run of one expert inside a rank's
+ * deficit region is one duplicate of that expert on that rank.
+ *
+ * Arithmetic: integers throughout the plan; maxvio in binary64 from exact
+ * integers; combine accumulates in binary32 with an explicit fused multiply-add
+ * in ascending k from +0.0f and rounds the accumulator to nearest-even bf16;
+ * the gradient reduce adds in binary32, home value first, then duplicates in
+ * ascending rank. Build with -ffp-contract=off so that no other fusion happens.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ST_BAD_ID = 1, ST_REPEAT_ID = 2, ST_OVER_B = 4 };
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+/* Caller-owned output arrays of the plan (sizes in the comments). */
+typedef struct oracle_plan_out {
+    int32_t *status;     /* [1] bit flags ST_*                               */
+    int64_t *maxT;       /* [1] largest expert count                         */
+    double  *maxvio;     /* [1] maxT*E/(R*S*K) - 1                            */
+    int32_t *T;          /* [E] assignments per expert                       */
+    int32_t *hoff;       /* [E] start of expert e in its home rank's list     */
+    int32_t *L;          /* [R] home load                                    */
+    int32_t *keep;       /* [R] min(L, S*K)                                  */
+    int32_t *O;          /* [R] overflow L - keep                            */
+    int32_t *D;          /* [R] deficit S*K - keep                           */
+    int32_t *Opre;       /* [R+1] exclusive prefix of O                      */
+    int32_t *Dpre;       /* [R+1] exclusive prefix of D                      */
+    int32_t *dst;        /* [R*S*K] slot r*S*K+s of entry a, or -1           */
+    int32_t *src;        /* [R*S*K] entry placed in slot, or -1              */
+    int32_t *n_dup;      /* [R]                                              */
+    int32_t *dup_expert; /* [R*dcap] -1 beyond n_dup                         */
+    int32_t *dup_start;  /* [R*dcap] first slot of the run, -1 beyond n_dup  */
+    int32_t *dup_count;  /* [R*dcap] rows of the run, 0 beyond n_dup         */
+    int32_t *seg_ptr;    /* [R*(G+dcap+1)] row offsets of rank segments, -1 pad */
+    int32_t *seg_expert; /* [R*(G+dcap)]   expert of each segment, -1 pad    */
+    int32_t *n_list;     /* [1] number of duplicates over all ranks          */
+    int32_t *list_expert;/* [pcap] duplicates ordered by (expert, rank)      */
+    int32_t *list_rank;  /* [pcap]                                           */
+    int32_t *list_b;     /* [pcap] index of the duplicate on its rank        */
+    int32_t *dup_ptr;    /* [E+1] CSR of the list over experts               */
+} oracle_plan_out;
+
+static int64_t find_deficit_rank(const int32_t *Dpre, int R, int64_t j)
+{
+    /* the unique r with Dpre[r] <= j < Dpre[r+1] (a plain linear walk) */
+    for (int r = 0; r < R; ++r)
+        if (Dpre[r] <= j && j < Dpre[r + 1]) return r;
+    return -1;
+}
+
+/* Returns 0, or -1 on inconsistent arguments. */
+int oracle_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
+                const int32_t *ids, int32_t dcap, int32_t pcap, oracle_plan_out *o)
+{
+    if (R <= 0 || E <= 0 || K <= 0 || S <= 0 || B < 0 || E % R != 0 || K > E) return -1;
+    const int64_t G = E / R, SK = (int64_t)S * K, N = (int64_t)R * S, NE = N * K;
+    int32_t status = 0;
+
+    /* Step 0: validate. Entries with an id outside [0,E) take part in nothing. */
+    for (int64_t g = 0; g < N; ++g)
+        for (int k = 0; k < K; ++k) {
+            int32_t e = ids[g * K + k];
+            if (e < 0 || e >= E) { status |= ST_BAD_ID; continue; }
+            for (int k2 = 0; k2 < k; ++k2)
+                if (ids[g * K + k2] == e) status |= ST_REPEAT_ID;
+        }
+
+    /* Step 1: histogram and maxvio. Tbar = R*S*K / E. */
+    for (int e = 0; e < E; ++e) o->T[e] = 0;
+    for (int64_t a = 0; a < NE; ++a)
+        if (ids[a] >= 0 && ids[a] < E) o->T[ids[a]] += 1;
+    int64_t maxT = 0;
+    for (int e = 0; e < E; ++e) if (o->T[e] > maxT) maxT = o->T[e];
+    *o->maxT = maxT;
+    *o->maxvio = (double)(maxT * (int64_t)E) / (double)NE - 1.0;
+
+    /* Step 2: home load. Expert e lives on rank e / G. */
+    for (int r = 0; r < R; ++r) {
+        int64_t acc = 0;
+        for (int64_t i = 0; i < G; ++i) {
+            o->hoff[r * G + i] = (int32_t)acc;
+            acc += o->T[r * G + i];
+        }
+        o->L[r] = (int32_t)acc;
+    }
+
+    /* Step 3a: water-fill quantities. */
+    o->Opre[0] = 0;
+    o->Dpre[0] = 0;
+    for (int r = 0; r < R; ++r) {
+        o->keep[r] = o->L[r] < SK ? o->L[r] : (int32_t)SK;
+        o->O[r] = o->L[r] - o->keep[r];
+        o->D[r] = (int32_t)SK - o->keep[r];
+        o->Opre[r + 1] = o->Opre[r] + o->O[r];
+        o->Dpre[r + 1] = o->Dpre[r] + o->D[r];
+    }
+
+    /* Step 3b: place every entry. pos = earlier entries of the same expert. */
+    for (int64_t s = 0; s < NE; ++s) o->src[s] = -1;
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!seen) return -1;
+    for (int64_t a = 0; a < NE; ++a) {
+        int32_t e = ids[a];
+        if (e < 0 || e >= E) { o->dst[a] = -1; continue; }
+        int64_t r = e / G;
+        int64_t h = (int64_t)o->hoff[e] + seen[e];
+        seen[e] += 1;
+        int64_t d, slot;
+        if (h < SK) {
+            d = r;
+            slot = h;
+        } else {
+            int64_t j = o->Opre[r] + (h - SK);
+            d = find_deficit_rank(o->Dpre, R, j);
+            slot = o->keep[d] + (j - o->Dpre[d]);
+        }
+        o->dst[a] = (int32_t)(d * SK + slot);
+        o->src[d * SK + slot] = (int32_t)a;
+    }
+    free(seen);
+
+    /* Step 3c: duplicates = maximal runs of one expert among the slots a rank
+       received beyond its kept rows. Unfilled slots (src == -1) end the walk. */
+    for (int64_t i = 0; i < (int64_t)R * dcap; ++i) {
+        o->dup_expert[i] = -1;
+        o->dup_start[i] = -1;
+        o->dup_count[i] = 0;
+    }
+    for (int r = 0; r < R; ++r) {
+        int32_t nd = 0;
+        int64_t s = o->keep[r];
+        while (s < SK && o->src[r * SK + s] >= 0) {
+            int32_t e = ids[o->src[r * SK + s]];
+            int64_t s0 = s;
+            while (s < SK && o->src[r * SK + s] >= 0 && ids[o->src[r * SK + s]] == e) ++s;
+            if (nd >= dcap) return -1;
+            o->dup_expert[(int64_t)r * dcap + nd] = e;
+            o->dup_start[(int64_t)r * dcap + nd] = (int32_t)s0;
+            o->dup_count[(int64_t)r * dcap + nd] = (int32_t)(s - s0);
+            ++nd;
+        }
+        o->n_dup[r] = nd;
+        if (nd > B) status |= ST_OVER_B;
+    }
+
+    /* Step 3d: per-rank segments: home experts in id order, then duplicates. */
+    const int64_t sp = G + dcap + 1, se = G + dcap;
+    for (int r = 0; r < R; ++r) {
+        for (int64_t i = 0; i < sp; ++i) o->seg_ptr[r * sp + i] = -1;
+        for (int64_t i = 0; i < se; ++i) o->seg_expert[r * se + i] = -1;
+        for (int64_t i = 0; i < G; ++i) {
+            int64_t st = o->hoff[r * G + i];
+            o->seg_ptr[r * sp + i] = (int32_t)(st < SK ? st : SK);
+            o->seg_expert[r * se + i] = (int32_t)(r * G + i);
+        }
+        int64_t end = o->keep[r];
+        for (int b = 0; b < o->n_dup[r]; ++b) {
+            o->seg_ptr[r * sp + G + b] = o->dup_start[(int64_t)r * dcap + b];
+            o->seg_expert[r * se + G + b] = o->dup_expert[(int64_t)r * dcap + b];
+            end = o->dup_start[(int64_t)r * dcap + b] + o->dup_count[(int64_t)r * dcap + b];
+        }
+        o->seg_ptr[r * sp + G + o->n_dup[r]] = (int32_t)end;
+    }
+
+    /* Step 3e: all duplicates ordered by (expert, rank), CSR over experts. */
+    for (int32_t p = 0; p < pcap; ++p) {
+        o->list_expert[p] = -1;
+        o->list_rank[p] = -1;
+        o->list_b[p] = -1;
+    }
+    int32_t p = 0;
+    for (int e = 0; e < E; ++e) {
+        o->dup_ptr[e] = p;
+        for (int r = 0; r < R; ++r)
+            for (int b = 0; b < o->n_dup[r]; ++b)
+                if (o->dup_expert[(int64_t)r * dcap + b] == e) {
+                    if (p >= pcap) return -1;
+                    o->list_expert[p] = e;
+                    o->list_rank[p] = r;
+                    o->list_b[p] = b;
+                    ++p;
+                }
+    }
+    o->dup_ptr[E] = p;
+    *o->n_list = p;
+    *o->status = status;
+    return 0;
+}
+
+/* Dispatch: recv[slot] = hidden[token of the entry placed there], byte for
+   byte. Only slots in [slot_lo, slot_hi) are written, into recv_window, whose
+   row 0 is slot slot_lo (this lets a caller stream the output by rank). */
+void oracle_dispatch(int64_t n_ent, int32_t K, int64_t row_bytes, const uint8_t *hidden,
+                     const int32_t *dst, int64_t slot_lo, int64_t slot_hi, uint8_t *recv_window)
+{
+    for (int64_t a = 0; a < n_ent; ++a) {
+        int64_t d = dst[a];
+        if (d < slot_lo || d >= slot_hi) continue;
+        memcpy(recv_window + (d - slot_lo) * row_bytes, hidden + (a / K) * row_bytes,
+               (size_t)row_bytes);
+    }
+}
+
+/* Replicate: dup_w[r][b] = expert_w[dup_expert[r][b]] for b < min(n_dup[r], B). */
+void oracle_replicate(int32_t R, int32_t B, int32_t dcap, const int32_t *n_dup,
+                      const int32_t *dup_expert, int64_t block_bytes,
+                      const uint8_t *expert_w, uint8_t *dup_w)
+{
+    for (int r = 0; r < R; ++r)
+        for (int b = 0; b < n_dup[r] && b < B; ++b)
+            memcpy(dup_w + ((int64_t)r * B + b) * block_bytes,
+                   expert_w + (int64_t)dup_expert[(int64_t)r * dcap + b] * block_bytes,
+                   (size_t)block_bytes);
+}
+
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round binary32 to the nearest bf16, ties to even; NaN stays a quiet NaN. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Combine: out[g] = sum_k w[g,k] * y[dst[g,k]], fp32 accumulation from +0.0f in
+   ascending k with fmaf, then stored as out_dtype. Entries with dst < 0 are
+   skipped. Tokens g in [0, n_tok). */
+void oracle_combine(int64_t n_tok, int32_t K, int64_t H, int32_t in_dtype, int32_t out_dtype,
+                    const void *y, const int32_t *dst, const float *w, void *out)
+{
+    for (int64_t g = 0; g < n_tok; ++g)
+        for (int64_t i = 0; i < H; ++i) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int64_t d = dst[g * K + k];
+                if (d < 0) continue;
+                float x = in_dtype == DT_BF16 ? bf16_to_f32(((const uint16_t *)y)[d * H + i])
+                                              : ((const float *)y)[d * H + i];
+                acc = fmaf(w[g * K + k], x, acc);
+            }
+            if (out_dtype == DT_BF16)
+                ((uint16_t *)out)[g * H + i] = f32_to_bf16_rne(acc);
+            else
+                ((float *)out)[g * H + i] = acc;
+        }
+}
+
+/* Reduce: for each expert e, home[e] = home[e] + dup_1 + dup_2 + ... over its
+   duplicates in list order (ascending rank), skipping duplicates with b >= B,
+   which have no slot. dup_grads is [R, B, n], home is [E, n], updated in place. */
+void oracle_reduce(int32_t E, int32_t B, int64_t n, const int32_t *dup_ptr,
+                   const int32_t *list_rank, const int32_t *list_b,
+                   const float *dup_grads, float *home)
+{
+    for (int e = 0; e < E; ++e)
+        for (int64_t i = 0; i < n; ++i) {
+            float v = home[(int64_t)e * n + i];
+            for (int32_t p = dup_ptr[e]; p < dup_ptr[e + 1]; ++p) {
+                if (list_b[p] >= B) continue;
+                v = v + dup_grads[((int64_t)list_rank[p] * B + list_b[p]) * n + i];
+            }
+            home[(int64_t)e * n + i] = v;
+        }
+}
+
+/* The rounding used by combine, exposed so tests can pin it to a library. */
+void oracle_f32_to_bf16(int64_t n, const float *x, uint16_t *y)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = f32_to_bf16_rne(x[i]);
+}
