@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the balanced expert-parallel hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic router output at the
+Kimi-K3-shaped layer (R=32 virtual ranks, E=896, K=16, S=4096, H=7168 bf16,
+B=28, weight blocks 3x7168x512 bf16): plan, replicate duplicate weights,
+dispatch, combine (identity expert: y = recv), reduce duplicate gradients.
+Inputs are resident in HBM before timing starts.
+
+Printed: ONE JSON line. `value` is dispatch+combine throughput in GB/s of
+algorithmic bytes (each token row read once, each slot written once, plus the
+index and weight arrays), measured with HIP events on the launch stream over the
+timed steps. `roofline` describes the dominant kernel; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "dispatch+combine GB/s (% of HBM peak) + plan latency µs, K3 shape, 1 GPU"
+KERNEL_SOURCES = ("token_dispatch_amd/csrc/move.hip", "token_dispatch_amd/csrc/plan.hip",
+                  "token_dispatch_amd/csrc/api.hip", "token_dispatch_amd/csrc/internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, n_mat, n_xm):
+    row = wl.row_bytes
+    d = wl.n_ent * row + wl.n_tok * row + 4 * wl.n_ent
+    c = wl.n_ent * row + wl.n_tok * row + 8 * wl.n_ent
+    rep = 2 * n_mat * wl.block_bytes
+    red = (n_mat + 2 * n_xm) * wl.block_elems * 4
+    plan = 12 * wl.n_ent
+    return {"dispatch": d, "combine": c, "replicate": rep, "reduce": red, "plan": plan}
+
+
+def traffic_for(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
+    """The oracle as it stands, single thread, on a bounded sample of the workload:
+    the full plan; dispatch of whole destination-rank windows (the oracle streams
+    its output by rank) for about half the budget; combine of the first n tokens
+    for the rest. Times are scaled to the whole workload (R windows; all tokens)."""
+    import numpy as np
+    import torch
+    import oracle
+
+    t0 = time.perf_counter()
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+    t_plan = time.perf_counter() - t0
+
+    hid = hidden_dev.view(wl.n_tok, wl.H).cpu().view(torch.int16).numpy().view(np.uint16)
+    t_disp, ranks = 0.0, 0
+    while ranks < wl.R and (ranks == 0 or t_disp < 0.5 * budget_s):
+        t0 = time.perf_counter()
+        oracle.dispatch(p, wl.K, hid, ranks * wl.SK, (ranks + 1) * wl.SK)
+        t_disp += time.perf_counter() - t0
+        ranks += 1
+    del hid
+
+    def gather(n):
+        dsel = p["dst"][:n * wl.K].astype(np.int64)
+        return y_dev.view(-1, wl.H)[torch.from_numpy(dsel).to(y_dev.device)].cpu() \
+            .view(torch.int16).numpy().view(np.uint16)
+
+    def comb(n, y_rows):
+        t0 = time.perf_counter()
+        oracle.combine(np.arange(n * wl.K, dtype=np.int32), wl.K, y_rows,
+                       w.reshape(-1)[:n * wl.K], wl.dtype, wl.dtype)
+        return time.perf_counter() - t0
+
+    probe = min(64, wl.n_tok)
+    per_tok = comb(probe, gather(probe)) / probe
+    left = max(0.0, budget_s - t_plan - t_disp)
+    n = int(min(wl.n_tok, 8192, max(probe, left / max(per_tok, 1e-9))))
+    t_comb = comb(n, gather(n))
+
+    nbytes = algorithmic_bytes(wl, 0, 0)
+    t_d_full = t_disp / ranks * wl.R
+    t_c_full = t_comb * wl.n_tok / n
+    gbs = (nbytes["dispatch"] + nbytes["combine"]) / (t_d_full + t_c_full) / 1e9
+    return {
+        "value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"full plan of {wl.n_ent} entries ({t_plan * 1e3:.1f} ms); dispatch of "
+                   f"{ranks} of {wl.R} destination-rank windows ({t_disp:.2f} s, scaled x"
+                   f"{wl.R / ranks:.2f}); combine of {n} of {wl.n_tok} tokens ({t_comb:.2f} s, "
+                   f"scaled x{wl.n_tok / n:.1f})"),
+        "plan_us": round(t_plan * 1e6, 1),
+        "measured_s": round(t_plan + t_disp + t_comb, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3",
+                    choices=["tiny", "uniform", "zipf", "k3", "decode"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import token_dispatch_amd as td
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[args.workload]
+    print(f"# setup {wl.name}: R={wl.R} E={wl.E} K={wl.K} S={wl.S} H={wl.H} B={wl.B}",
+          file=sys.stderr, flush=True)
+    ids, w = W.make_routing(wl, args.seed)
+    dims = td.Dims(wl.R, wl.E, wl.K, wl.S, wl.B, wl.dtype, wl.H)
+    ids_d = torch.from_numpy(ids).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
+    hidden = W.make_hidden(wl, args.seed, dev)
+    recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hidden.dtype, device=dev)
+    out = torch.empty_like(hidden)
+    expert_w = W.make_expert_weights(wl, args.seed, dev)
+    dup_w = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=expert_w.dtype, device=dev)
+    dup_g, home_g = W.make_grads(wl, args.seed, dev)
+    plan_buf = td.new_plan_buffer(dims, dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    print("# inputs resident", file=sys.stderr, flush=True)
+
+    ops = ["plan", "replicate", "dispatch", "combine", "reduce"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        td.moonep_plan(dims, ids_d, plan_buf)
+        if ev:
+            ev[1].record(stream)
+        td.moonep_replicate(dims, plan_buf, expert_w, dup_w, wl.block_bytes)
+        if ev:
+            ev[2].record(stream)
+        td.moonep_dispatch(dims, plan_buf, hidden, recv)
+        if ev:
+            ev[3].record(stream)
+        td.moonep_combine(dims, plan_buf, recv, w_d, out)
+        if ev:
+            ev[4].record(stream)
+        td.moonep_reduce_dup_grads(dims, plan_buf, dup_g, home_g, wl.block_elems)
+        if ev:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+             for j, op in enumerate(ops)}
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    v = td.plan_views(dims, plan_buf)
+    n_dup = v["n_dup"].cpu().numpy()
+    n_mat = int(np.minimum(n_dup, wl.B).sum())
+    nl = int(v["n_list"][0])
+    lb = v["list_b"][:nl].cpu().numpy()
+    le = v["list_expert"][:nl].cpu().numpy()
+    n_xm = int(np.unique(le[lb < wl.B]).size)
+    seg = v["seg_ptr"].cpu().numpy()
+    rows = seg[np.arange(wl.R), wl.G + n_dup]
+    rank_maxvio_after = float(rows.max()) / wl.SK - 1.0
+    status = int(v["status"][0])
+    maxvio = float(v["maxvio"][0])
+    nbytes = algorithmic_bytes(wl, n_mat, n_xm)
+    gbs = {op: nbytes[op] / (op_ms[op] * 1e-3) / 1e9 for op in ops}
+    dc_bytes = nbytes["dispatch"] + nbytes["combine"]
+    dc_ms = op_ms["dispatch"] + op_ms["combine"]
+    value = dc_bytes / (dc_ms * 1e-3) / 1e9
+
+    dom = max(("dispatch", "combine"), key=lambda o: op_ms[o])
+    src_hash = kernel_source_hash()
+    traffic = traffic_for(dom, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(gbs[dom], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs[dom] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom, "algorithmic_bytes_per_launch": nbytes[dom],
+                "avg_launch_ms": round(op_ms[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, ids, w, hidden, recv, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if wl.dtype == W.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: R={wl.R} virtual ranks, E={wl.E}, K={wl.K}, "
+                               f"S={wl.S}, H={wl.H}, B={wl.B}, weight block "
+                               f"{'x'.join(map(str, wl.block_shape))}",
+                   "routing": wl.routing, "seed": args.seed, "parallelism": "ep (virtual, 1 GPU)"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "plan_us": round(op_ms["plan"] * 1e3, 2),
+        "op_ms": {k: round(x, 4) for k, x in op_ms.items()},
+        "op_gbs": {k: round(x, 1) for k, x in gbs.items()},
+        "maxvio_before": round(maxvio, 4), "rank_maxvio_after": rank_maxvio_after,
+        "dups_per_rank_max": int(n_dup.max()), "dups_total": int(n_dup.sum()), "B": wl.B,
+        "status": status, "kernel_source_hash": src_hash,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

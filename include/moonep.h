@@ -1,0 +1,216 @@
+/*
+ * moonep.h -- C ABI of the balanced expert-parallel hot path for MI355X (gfx950).
+ *
+ * The method (MoonEP, Moonshot AI, as described on news.hamidun.com EN,
+ * "How MoonEP works"): every expert-parallel rank receives exactly S x K routed
+ * (token, k) assignments whatever the routing skew, by scheduling a few
+ * duplicate experts online from the current router output; duplicates are
+ * fetched before the expert computation and their gradients are reduced back to
+ * the home ranks on the backward pass. Tokens are written straight into static
+ * buffers at positions grouped by expert, so no shape depends on the routing and
+ * no call needs the host ("Why this matters to engineers", same page).
+ *
+ * On one GPU the R ranks are virtual: rank r's share of every [R, ...] array is
+ * its slice [r], and moving a row between ranks is a copy between slices.
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or keeps a pointer after a call returns, and never
+ *     synchronises with the host: every call only enqueues kernels on `stream`
+ *     (a hipStream_t passed as void*; NULL is the default stream).
+ *   - Every pointer must be non-NULL and 16-byte aligned.
+ *   - Arrays are dense, row-major, in the shapes given below. Indices are int32.
+ *   - Synchronous errors are the return value (checked on the host before any
+ *     launch; nothing is enqueued on error). Errors that depend on data -- bad
+ *     expert ids, more duplicates than B -- are bits in the plan's status word,
+ *     written on the device; the caller reads it when it chooses to synchronise.
+ *   - Calls that share a plan buffer must be ordered (same stream, or events).
+ *     Calls on different plan buffers and outputs are independent.
+ */
+#ifndef MOONEP_H
+#define MOONEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of hidden / expert-output rows. */
+enum { MOONEP_F32 = 0, MOONEP_BF16 = 1 };
+
+/* Return values. */
+enum {
+    MOONEP_OK = 0,
+    MOONEP_ERR_DIMS = -1,   /* dims outside the supported range (see moonep_dims)      */
+    MOONEP_ERR_PTR = -2,    /* NULL or not 16-byte aligned pointer                      */
+    MOONEP_ERR_HIP = -3,    /* the HIP runtime refused a launch (hipGetLastError)      */
+    MOONEP_ERR_SIZE = -4    /* a byte/element count argument is inconsistent           */
+};
+
+/* Bits of the plan's status word. */
+enum {
+    MOONEP_STATUS_BAD_ID = 1,    /* an id outside [0, E): that entry is dropped (dst = -1) */
+    MOONEP_STATUS_REPEAT_ID = 2, /* one token names the same expert twice; the plan is
+                                    still well defined, ties broken by (token, k)        */
+    MOONEP_STATUS_OVER_B = 4     /* some rank needs more than B duplicates; the plan is
+                                    complete, but only duplicates b < B have a slot in
+                                    replicate / reduce                                  */
+};
+
+/*
+ * Problem size of one MoE layer step (news.hamidun.com EN, "How MoonEP works":
+ * S input tokens per rank, K experts per token; "Key facts about the release":
+ * B = E/R for training, 3-4 for inference).
+ *   R      ranks (virtual on one GPU), 1 <= R <= 1024
+ *   E      experts, R <= E <= 1024, E % R == 0; expert e lives on rank e / (E/R)
+ *   K      experts per token, 1 <= K <= min(E, 64)
+ *   S      tokens per rank, S >= 1, R*S*K < 2^31
+ *   B      duplicate-expert slots per rank (the [R, B, ...] shape of the
+ *          duplicate weight and gradient buffers), B >= 0
+ *   dtype  MOONEP_F32 or MOONEP_BF16: element type of hidden / recv / y / out
+ *   H      hidden size; H * element size must be a multiple of 16 bytes
+ */
+typedef struct moonep_dims {
+    int32_t R, E, K, S, B;
+    int32_t dtype;
+    int64_t H;
+} moonep_dims;
+
+/*
+ * Layout of the plan buffer: ONE caller-allocated device buffer of `bytes`
+ * bytes holding every plan array at the given byte offsets (all 256-byte
+ * aligned). The sizes depend on the dims only. G = E/R, SK = S*K.
+ *
+ *   status      int32 [1]          MOONEP_STATUS_* bits
+ *   maxT        int32 [1]          largest expert count
+ *   maxvio      double [1]         maxT * E / (R*S*K) - 1, binary64 from exact integers
+ *   T           int32 [E]          assignments routed to each expert
+ *   hoff        int32 [E]          start of expert e in its home rank's (expert, token) list
+ *   L           int32 [R]          home load: sum of T over the rank's G home experts
+ *   keep        int32 [R]          min(L, SK): home rows kept on the rank
+ *   O, D        int32 [R]          overflow L - keep and deficit SK - keep
+ *   Opre, Dpre  int32 [R+1]        exclusive prefix sums of O and D
+ *   dst         int32 [R*S*K]      slot of entry a = (r*S + s)*K + k, as rank*SK + row;
+ *                                  -1 for a dropped entry
+ *   src         int32 [R*S*K]      inverse: entry held by each slot, -1 if unfilled
+ *   n_dup       int32 [R]          duplicates held by each rank (may exceed B)
+ *   dup_expert  int32 [R, dcap]    expert of duplicate b of rank r (-1 beyond n_dup)
+ *   dup_start   int32 [R, dcap]    its first row on the rank (-1 beyond n_dup)
+ *   dup_count   int32 [R, dcap]    its rows (0 beyond n_dup)
+ *   seg_ptr     int32 [R, G+dcap+1] row offsets of the rank's expert segments: home
+ *                                  experts in id order, then duplicates; G+n_dup+1 used,
+ *                                  -1 beyond
+ *   seg_expert  int32 [R, G+dcap]  expert of each segment, -1 beyond
+ *   n_list      int32 [1]          number of duplicates over all ranks
+ *   list_expert, list_rank, list_b  int32 [pcap]  every duplicate, ordered by
+ *                                  (expert, rank); -1 beyond n_list
+ *   dup_ptr     int32 [E+1]        CSR of that list over experts
+ * The remaining offsets are workspace of the plan kernels; callers must not
+ * rely on their contents.
+ */
+typedef struct moonep_layout {
+    int64_t bytes;
+    int32_t dcap;          /* max(1, min(SK, E - G)): most duplicates one rank can hold */
+    int32_t pcap;          /* E + R: room for the global duplicate list                 */
+    int32_t n_tiles;       /* token tiles of the plan kernels                           */
+    int32_t tile_tokens;   /* tokens per tile                                           */
+    int64_t status, maxT, maxvio, T, hoff, L, keep, O, D, Opre, Dpre, dst, src;
+    int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
+    int64_t n_list, list_expert, list_rank, list_b, dup_ptr;
+    int64_t ws_tile_counts, ws_tile_status, ws_mat_pre, ws_xlist, ws_n_x;
+} moonep_layout;
+
+/* Fills *out for dims. Pure host computation. Returns MOONEP_OK or
+   MOONEP_ERR_DIMS / MOONEP_ERR_PTR (out == NULL). */
+int moonep_plan_layout(const moonep_dims *dims, moonep_layout *out);
+
+/*
+ * moonep_plan -- the online redundant-expert plan of one step
+ * (news.hamidun.com EN, "How MoonEP works" and "Why expert parallelism is
+ * needed"; blog.schoergendorfer.com, "The problem MoonEP targets" for maxvio).
+ *
+ *   topk_ids  int32 [R, S, K] device, read only: the router's expert ids
+ *   plan_buf  device buffer of moonep_plan_layout().bytes bytes, written
+ *
+ * Steps: expert histogram T and maxvio; home load L per rank; the water-fill:
+ * each rank keeps the first min(L, S*K) of its home assignments in (expert,
+ * token, k) order, the rest -- ordered by (home rank, expert, token, k) -- fills
+ * the deficit slots of the ranks in rank order by prefix sums; each maximal run
+ * of one expert inside a rank's received rows is one duplicate of that expert on
+ * that rank. With valid ids every rank gets exactly S*K rows, grouped by expert.
+ * The result depends on the ids only (B only sets MOONEP_STATUS_OVER_B) and is
+ * bit-for-bit deterministic.
+ */
+int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf, void *stream);
+
+/*
+ * moonep_dispatch -- zero-copy scatter of token rows into the static,
+ * expert-grouped receive buffer (news.hamidun.com EN, "Why this matters to
+ * engineers": tokens written straight into positions grouped by expert).
+ *
+ *   plan_buf  read: dst
+ *   hidden    [R, S, H] of dims->dtype, read; each row is read once
+ *   recv      [R, S*K, H] of dims->dtype, written: recv[dst[a]] = hidden[a / K]
+ *             byte for byte; every filled slot is written exactly once, unfilled
+ *             slots (only after MOONEP_STATUS_BAD_ID) are left untouched.
+ */
+int moonep_dispatch(const moonep_dims *dims, const void *plan_buf, const void *hidden,
+                    void *recv, void *stream);
+
+/*
+ * moonep_replicate -- fetch duplicate expert weights from home before the expert
+ * computation (news.hamidun.com EN, "How MoonEP works": duplicates are prefetched).
+ *
+ *   expert_w     [E, block_bytes] read: each expert's weights as opaque bytes
+ *   dup_w        [R, B, block_bytes] written: dup_w[r][b] = expert_w[dup_expert[r][b]]
+ *                for b < min(n_dup[r], B); other slots are left untouched
+ *   block_bytes  > 0, multiple of 16
+ * With B == 0 there is nothing to copy: the call checks dims and block_bytes,
+ * enqueues nothing, and the pointers may be NULL.
+ */
+int moonep_replicate(const moonep_dims *dims, const void *plan_buf, const void *expert_w,
+                     void *dup_w, int64_t block_bytes, void *stream);
+
+/*
+ * moonep_combine -- weighted sum of each token's K expert outputs back into the
+ * token's row (the router sends each token to K experts, news.hamidun.com EN,
+ * "Why expert parallelism is needed").
+ *
+ *   y          [R, S*K, H] of dims->dtype, read: expert outputs in recv layout
+ *   topk_w     float32 [R, S, K], read: router weights
+ *   out        [R, S, H] of out_dtype, written:
+ *              out[g] = sum over k = 0..K-1 of topk_w[g,k] * y[dst[g*K+k]],
+ *              accumulated in binary32 from +0.0 with a fused multiply-add in
+ *              ascending k, then stored (bf16: round to nearest even).
+ *              Dropped entries (dst = -1) contribute nothing.
+ *   out_dtype  MOONEP_F32 or MOONEP_BF16
+ */
+int moonep_combine(const moonep_dims *dims, const void *plan_buf, const void *y,
+                   const float *topk_w, void *out, int32_t out_dtype, void *stream);
+
+/*
+ * moonep_reduce_dup_grads -- reduce duplicate-expert gradients back to the home
+ * experts on the backward pass (news.hamidun.com EN, "How MoonEP works").
+ *
+ *   dup_grads    float32 [R, B, block_elems], read
+ *   home_grads   float32 [E, block_elems], updated in place: for every expert e
+ *                with duplicates, home_grads[e] = home_grads[e] + dup_1 + dup_2 ...
+ *                over its duplicates b < B in ascending rank, binary32 adds in
+ *                that fixed order. Experts without duplicates are not touched.
+ *   block_elems  > 0, multiple of 4
+ * With B == 0 there is nothing to add: the call checks dims and block_elems,
+ * enqueues nothing, and the pointers may be NULL.
+ */
+int moonep_reduce_dup_grads(const moonep_dims *dims, const void *plan_buf,
+                            const float *dup_grads, float *home_grads, int64_t block_elems,
+                            void *stream);
+
+/* Text of a return value. Never NULL; the string is static. */
+const char *moonep_strerror(int rc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOONEP_H */

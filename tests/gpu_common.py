@@ -1,0 +1,63 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and read
+results back for comparison with the oracle. Nothing here computes the method."""
+import sys
+
+import numpy as np
+
+PLAN_INT_KEYS = ("status", "T", "hoff", "L", "keep", "O", "D", "Opre", "Dpre", "dst", "src",
+                 "n_dup", "dup_expert", "dup_start", "dup_count", "seg_ptr", "seg_expert",
+                 "n_list", "list_expert", "list_rank", "list_b", "dup_ptr")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dims_for(td, R, E, K, S, B, H, dtype):
+    return td.Dims(R, E, K, S, B, dtype, H)
+
+
+def run_plan(td, dims, ids_np, dev, plan_buf=None):
+    import torch
+    if plan_buf is None:
+        plan_buf = td.new_plan_buffer(dims, dev)
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
+    td.moonep_plan(dims, ids_d, plan_buf)
+    torch.cuda.synchronize()
+    return plan_buf, ids_d
+
+
+def read_plan(td, dims, plan_buf):
+    v = td.plan_views(dims, plan_buf)
+    out = {k: t.cpu().numpy() for k, t in v.items()}
+    out["dcap"] = out["dup_expert"].shape[1]
+    return out
+
+
+def assert_plan_equal(gpu, orc):
+    """Bit-exact comparison of every public plan array."""
+    for k in PLAN_INT_KEYS:
+        g = np.asarray(gpu[k]).reshape(-1).astype(np.int64)
+        o = np.asarray(orc[k]).reshape(-1).astype(np.int64)
+        if not np.array_equal(g, o):
+            bad = np.nonzero(g != o)[0] if g.shape == o.shape else None
+            raise AssertionError(
+                f"plan array {k} differs: shapes {g.shape} vs {o.shape}; "
+                f"first mismatches at {None if bad is None else bad[:8].tolist()}: "
+                f"gpu {None if bad is None else g[bad[:8]].tolist()} "
+                f"oracle {None if bad is None else o[bad[:8]].tolist()}")
+    assert int(np.asarray(gpu["maxT"]).reshape(-1)[0]) == int(np.asarray(orc["maxT"]).reshape(-1)[0])
+    gm = np.asarray(gpu["maxvio"]).reshape(-1)[:1].view(np.uint64)
+    om = np.asarray(orc["maxvio"]).reshape(-1)[:1].view(np.uint64)
+    assert np.array_equal(gm, om), "maxvio bits differ"
+
+
+def bf16_bits(t):
+    """uint16 numpy view of a bf16 torch tensor (CPU copy)."""
+    import torch
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_bits(t):
+    return t.detach().contiguous().cpu().numpy().view(np.uint32)

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+- the library loads and exports every function include/moonep.h declares
+- the plan layout: sizes follow the dims only, arrays are 256-byte aligned and
+  disjoint, dcap and pcap are as documented
+- argument errors are returned synchronously, before anything is enqueued
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moonep.h")
+
+
+@pytest.fixture(scope="module")
+def td():
+    import token_dispatch_amd as td
+    return td
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moonep_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(td):
+    names = _declared_functions()
+    assert set(names) == set(td.ENTRY_POINTS)
+    lib = ctypes.CDLL(td.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _dims(td, R=32, E=896, K=16, S=4096, B=28, dtype=1, H=7168):
+    return td.Dims(R, E, K, S, B, dtype, H)
+
+
+@pytest.mark.parametrize("shape", [(32, 896, 16, 4096, 28, 1, 7168), (4, 16, 2, 64, 4, 0, 128),
+                                   (64, 896, 16, 128, 4, 1, 7168), (1, 8, 8, 3, 0, 0, 4),
+                                   (1024, 1024, 64, 1, 1, 1, 8)])
+def test_layout(td, shape):
+    d = td.Dims(*shape)
+    lay = td.moonep_plan_layout(d)
+    R, E, K, S, B = shape[:5]
+    G, SK = E // R, S * K
+    assert lay.dcap == max(1, min(SK, E - G))
+    assert lay.pcap == E + R
+    assert lay.tile_tokens == 4096 // K
+    assert lay.n_tiles == -(-(R * S) // lay.tile_tokens)
+    sizes = {"status": 4, "maxT": 4, "maxvio": 8, "T": 4 * E, "hoff": 4 * E, "L": 4 * R,
+             "keep": 4 * R, "O": 4 * R, "D": 4 * R, "Opre": 4 * (R + 1), "Dpre": 4 * (R + 1),
+             "dst": 4 * R * SK, "src": 4 * R * SK, "n_dup": 4 * R,
+             "dup_expert": 4 * R * lay.dcap, "dup_start": 4 * R * lay.dcap,
+             "dup_count": 4 * R * lay.dcap, "seg_ptr": 4 * R * (G + lay.dcap + 1),
+             "seg_expert": 4 * R * (G + lay.dcap), "n_list": 4, "list_expert": 4 * lay.pcap,
+             "list_rank": 4 * lay.pcap, "list_b": 4 * lay.pcap, "dup_ptr": 4 * (E + 1),
+             "ws_tile_counts": 4 * lay.n_tiles * E, "ws_tile_status": 4 * lay.n_tiles,
+             "ws_mat_pre": 4 * (R + 1), "ws_xlist": 4 * E, "ws_n_x": 4}
+    spans = sorted((getattr(lay, k), getattr(lay, k) + v) for k, v in sizes.items())
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a0 % 256 == 0 and a1 <= b0
+    assert spans[-1][1] <= lay.bytes
+    # same dims, same layout (static shapes)
+    assert td.moonep_plan_layout(td.Dims(*shape)).bytes == lay.bytes
+
+
+@pytest.mark.parametrize("bad", [
+    dict(R=0), dict(R=1025, E=2050), dict(E=900), dict(E=1025 * 1), dict(K=0), dict(K=65, E=896),
+    dict(K=897), dict(S=0), dict(B=-1), dict(dtype=2), dict(H=0), dict(H=7), dict(dtype=0, H=6),
+    dict(R=32, S=1 << 23),
+])
+def test_invalid_dims_rejected(td, bad):
+    kw = dict(R=32, E=896, K=16, S=4096, B=28, dtype=1, H=7168)
+    kw.update(bad)
+    d = td.Dims(kw["R"], kw["E"], kw["K"], kw["S"], kw["B"], kw["dtype"], kw["H"])
+    lay = td.Layout()
+    assert td._lib.moonep_plan_layout(ctypes.byref(d), ctypes.byref(lay)) == -1
+    for fn, args in [("moonep_plan", (None, None, None)),
+                     ("moonep_dispatch", (None, None, None, None)),
+                     ("moonep_replicate", (None, None, None, 16, None)),
+                     ("moonep_combine", (None, None, None, None, 1, None)),
+                     ("moonep_reduce_dup_grads", (None, None, None, 4, None))]:
+        assert getattr(td._lib, fn)(ctypes.byref(d), *args) == -1, fn
+
+
+def test_pointer_and_size_errors(td):
+    d = _dims(td)
+    lib = td._lib
+    ok = ctypes.c_void_p(1 << 20)         # aligned, never dereferenced: calls fail first
+    mis = ctypes.c_void_p((1 << 20) + 8)  # not 16-byte aligned
+    assert lib.moonep_plan_layout(ctypes.byref(d), None) == -2
+    assert lib.moonep_plan(None, ok, ok, None) == -2
+    assert lib.moonep_plan(ctypes.byref(d), None, ok, None) == -2
+    assert lib.moonep_plan(ctypes.byref(d), mis, ok, None) == -2
+    assert lib.moonep_dispatch(ctypes.byref(d), ok, mis, ok, None) == -2
+    assert lib.moonep_combine(ctypes.byref(d), ok, ok, ok, mis, 1, None) == -2
+    assert lib.moonep_combine(ctypes.byref(d), ok, ok, ok, ok, 3, None) == -1
+    assert lib.moonep_replicate(ctypes.byref(d), ok, ok, ok, 24, None) == -4
+    assert lib.moonep_replicate(ctypes.byref(d), ok, ok, ok, 0, None) == -4
+    assert lib.moonep_reduce_dup_grads(ctypes.byref(d), ok, ok, ok, 6, None) == -4
+    assert lib.moonep_reduce_dup_grads(ctypes.byref(d), ok, mis, ok, 8, None) == -2
+    d0 = _dims(td, B=0)
+    assert lib.moonep_replicate(ctypes.byref(d0), None, None, None, 16, None) == 0
+    assert lib.moonep_reduce_dup_grads(ctypes.byref(d0), None, None, None, 4, None) == 0
+    for rc in (0, -1, -2, -3, -4, 5):
+        assert td.moonep_strerror(rc)
+
+
+def test_binding_checks_tensors(td):
+    import torch
+    d = td.Dims(4, 16, 2, 64, 4, 0, 128)
+    with pytest.raises(ValueError):
+        td.moonep_plan(d, torch.zeros(512, dtype=torch.int32), torch.zeros(10, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        td.moonep_plan(d, [1, 2], None)

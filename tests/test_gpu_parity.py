@@ -1,0 +1,355 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Plan arrays, dispatch and replicate bytes are compared bit for bit. Combine and
+reduce accumulate in binary32 in the same fixed order as the oracle, so they are
+compared bit for bit too, which is stricter than the 1e-5 relative bound the
+path promises (that bound is also asserted on the fp32 combine output).
+
+Small shapes are compared element by element; they span several plan tiles with
+a ragged last tile and rows whose 16-byte chunk count does not fill the lanes.
+The five workload shapes are run at full size in the launch configuration the
+benchmark times: the whole plan is compared, dispatch and replicate are checked
+everywhere against the oracle's plan tables, combine and reduce on sampled
+tokens / experts that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, read_plan, run_plan,
+                              say)
+from tests.invariants import check_plan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def td():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU parity tests need a GPU")
+    import token_dispatch_amd as td
+    torch.cuda.set_device(DEV)
+    return td
+
+
+def _wl(name, R, E, K, S, B, H, dtype, skew, block=(8, 36)):
+    return W.Workload(name, R=R, E=E, K=K, S=S, H=H, dtype=dtype, B=B, block_shape=block,
+                      block_dtype=W.BF16, routing="bias", bias_std=skew)
+
+
+SMALL = [
+    # several tiles with a ragged tail; fp32 rows of 18 chunks (ragged lanes)
+    _wl("tiles_ragged", 4, 32, 4, 3001, 4, 72, W.F32, 2.0),
+    # bf16 rows of 125 chunks: two chunks per lane, ragged
+    _wl("bf16_ragged_row", 8, 64, 8, 700, 8, 1000, W.BF16, 1.5),
+    _wl("k1", 2, 8, 1, 5000, 2, 64, W.BF16, 3.0),
+    # one home expert per rank, 16-byte rows
+    _wl("g1", 6, 6, 2, 333, 3, 8, W.BF16, 2.0),
+    # a single rank: nothing can overflow; no duplicate slots
+    _wl("r1", 1, 16, 4, 2000, 0, 32, W.F32, 1.0),
+    _wl("k64", 2, 128, 64, 300, 64, 256, W.BF16, 1.0),
+    _wl("s1", 16, 64, 8, 1, 4, 128, W.BF16, 3.0),
+    # rows longer than one 16-chunk-per-lane segment (two segments)
+    _wl("long_row", 2, 16, 2, 200, 2, 12288, W.BF16, 2.0),
+    _wl("e1024", 8, 1024, 8, 600, 128, 64, W.BF16, 2.0),
+    # fp32 rows and a larger fp32 weight block
+    _wl("f32_wide", 4, 16, 2, 1000, 4, 1024, W.F32, 2.5, block=(3, 64, 64)),
+    # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
+    W.WORKLOADS["tiny"],
+]
+
+
+def _dims(td, wl):
+    return td.Dims(wl.R, wl.E, wl.K, wl.S, wl.B, wl.dtype, wl.H)
+
+
+def _host_rows(t):
+    """Bits of a row tensor as numpy (uint16 for bf16, float32 for fp32)."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.detach().contiguous().cpu().numpy()
+
+
+def _full_case(td, wl, ids, w, seed):
+    """Everything compared element by element (small shapes only)."""
+    dims = _dims(td, wl)
+    say(f"case {wl.name}: {dims}")
+    plan_buf, _ = run_plan(td, dims, ids, DEV)
+    g = read_plan(td, dims, plan_buf)
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+    assert_plan_equal(g, p)
+    valid = bool(np.all((ids >= 0) & (ids < wl.E)))
+    check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g, valid_input=valid)
+
+    hidden = W.make_hidden(wl, seed)
+    hid_d = hidden.to(DEV)
+    recv = torch.full((wl.R, wl.SK, wl.H), 7.0, dtype=hid_d.dtype, device=DEV)
+    td.moonep_dispatch(dims, plan_buf, hid_d, recv)
+    torch.cuda.synchronize()
+    hid_h = _host_rows(hidden).reshape(wl.n_tok, wl.H)
+    want = oracle.dispatch(p, wl.K, hid_h)
+    got = _host_rows(recv).reshape(-1, wl.H)
+    filled = p["src"] >= 0
+    assert np.array_equal(got[filled].view(np.uint8), want[filled].view(np.uint8)), "dispatch"
+
+    # combine reads expert outputs y; here y = a fresh seeded tensor in recv layout
+    y = W.make_expert_out(wl, seed)
+    y_d = y.to(DEV)
+    w_d = torch.from_numpy(w).to(DEV)
+    y_h = _host_rows(y).reshape(-1, wl.H)
+    for od in (W.F32, W.BF16):
+        out = torch.empty((wl.R, wl.S, wl.H), dtype=W.torch_dtype(od), device=DEV)
+        td.moonep_combine(dims, plan_buf, y_d, w_d, out, od)
+        torch.cuda.synchronize()
+        want = oracle.combine(p["dst"], wl.K, y_h, w, wl.dtype, od)
+        got = _host_rows(out).reshape(-1, wl.H)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"combine out_dtype={od}"
+        if od == W.F32:
+            rel = np.abs(got.astype(np.float64) - want) / np.maximum(np.abs(want), 1e-30)
+            assert np.all(rel <= 1e-5)
+
+    # replicate and reduce
+    ew = W.make_expert_weights(wl, seed)
+    ew_d = ew.to(DEV)
+    dup_w = torch.zeros((wl.R, wl.B) + tuple(wl.block_shape), dtype=ew.dtype, device=DEV)
+    td.moonep_replicate(dims, plan_buf, ew_d, dup_w, wl.block_bytes)
+    dg, hg = W.make_grads(wl, seed)
+    hg_d = hg.to(DEV)
+    td.moonep_reduce_dup_grads(dims, plan_buf, dg.to(DEV), hg_d, wl.block_elems)
+    torch.cuda.synchronize()
+    want_w = oracle.replicate(p, wl.B, bf16_bits(ew) if ew.dtype == torch.bfloat16 else ew.numpy())
+    got_w = _host_rows(dup_w)
+    for r in range(wl.R):
+        for b in range(wl.B):
+            if b < int(p["n_dup"][r]):
+                assert np.array_equal(got_w[r, b].view(np.uint8), want_w[r, b].view(np.uint8))
+            else:
+                assert not np.any(got_w[r, b].view(np.uint8)), "an unused slot was written"
+    want_h = oracle.reduce_dup_grads(p, wl.B, dg.numpy(), hg.numpy())
+    assert np.array_equal(f32_bits(hg_d), want_h.view(np.uint32)), "reduce"
+    return g
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes_elementwise(td, wl):
+    ids, w = W.make_routing(wl, seed=3)
+    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3)
+
+
+def test_hand_worked_examples_on_gpu(td):
+    import glob
+    import json
+    import os
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden",
+                                              "plan_example*.json"))):
+        ex = json.load(open(path))
+        dims = td.Dims(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], W.F32, 4)
+        say(f"golden {os.path.basename(path)}")
+        ids = np.array(ex["ids"], np.int32)
+        plan_buf, _ = run_plan(td, dims, ids, DEV)
+        g = read_plan(td, dims, plan_buf)
+        SK = ex["S"] * ex["K"]
+        x = ex["expect"]
+        assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
+        assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
+        assert float(g["maxvio"][0]) == x["maxvio"]
+        assert_plan_equal(g, oracle.plan(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], ids))
+
+
+def test_invalid_and_repeated_ids(td):
+    wl = _wl("bad_ids", 4, 32, 4, 1500, 4, 64, W.BF16, 2.0)
+    rng = np.random.default_rng(17)
+    ids, w = W.make_routing(wl, seed=5)
+    ids = ids.reshape(-1).copy()
+    w = w.reshape(-1)
+    bad = rng.choice(ids.size, 40, replace=False)
+    ids[bad] = rng.choice([-1, -100, wl.E, wl.E + 7], 40)
+    g = _full_case(td, wl, ids, w, 5)
+    assert int(g["status"][0]) & 1
+    ids2, w2 = W.make_routing(wl, seed=6)
+    ids2 = ids2.reshape(-1, wl.K).copy()
+    t = rng.choice(wl.n_tok, 25, replace=False)
+    ids2[t, 2] = ids2[t, 0]
+    g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6)
+    assert int(g["status"][0]) & 2
+
+
+def test_extreme_skew_and_balance(td):
+    # every token picks the same K experts, all homed on rank 0
+    wl = _wl("one_hot_rank", 8, 64, 8, 1000, 8, 64, W.BF16, 0.0)
+    ids = np.tile(np.arange(8, dtype=np.int32), wl.n_tok)
+    w = np.full(ids.size, 1.0 / 8, np.float32)
+    g = _full_case(td, wl, ids, w, 1)
+    assert int(g["n_dup"].sum()) > 0 and int(g["L"][0]) == wl.n_ent
+    # perfectly balanced routing: no overflow, no duplicates
+    wl = _wl("balanced", 4, 16, 4, 256, 2, 64, W.BF16, 0.0)
+    ids = (np.arange(wl.n_ent) % wl.E).astype(np.int32)
+    w = np.full(ids.size, 0.25, np.float32)
+    g = _full_case(td, wl, ids, w, 2)
+    assert int(g["n_dup"].sum()) == 0 and float(g["maxvio"][0]) == 0.0
+
+
+def test_identity_expert_mean_returns_hidden(td):
+    """y = recv and w = 1/K with K a power of two: combine gives back hidden bit for bit."""
+    wl = _wl("identity", 8, 64, 8, 900, 8, 512, W.BF16, 2.0)
+    dims = _dims(td, wl)
+    ids, _ = W.make_routing(wl, seed=2)
+    plan_buf, _ = run_plan(td, dims, ids, DEV)
+    hid = W.make_hidden(wl, 2).to(DEV)
+    recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hid.dtype, device=DEV)
+    out = torch.empty_like(hid)
+    w = torch.full((wl.R, wl.S, wl.K), 1.0 / wl.K, dtype=torch.float32, device=DEV)
+    td.moonep_dispatch(dims, plan_buf, hid, recv)
+    td.moonep_combine(dims, plan_buf, recv, w, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), hid.view(torch.int16))
+
+
+def test_deterministic_and_stream_ordered(td):
+    wl = W.WORKLOADS["zipf"].replace(S=2048)
+    dims = _dims(td, wl)
+    ids, _ = W.make_routing(wl, seed=1)
+    s = torch.cuda.Stream(DEV)
+    bufs = []
+    for _ in range(3):
+        pb = td.new_plan_buffer(dims, DEV)
+        with torch.cuda.stream(s):
+            ids_d = torch.from_numpy(ids).to(DEV, non_blocking=False)
+            td.moonep_plan(dims, ids_d, pb, stream=s)
+        bufs.append(pb)
+    torch.cuda.synchronize()
+    a = read_plan(td, dims, bufs[0])
+    for pb in bufs[1:]:
+        assert_plan_equal(read_plan(td, dims, pb), a)
+
+
+def test_plan_buffer_reuse_across_shapes(td):
+    """A plan buffer first used for a larger problem gives the same plan for a
+    smaller one (no stale state leaks into the result)."""
+    big = _wl("big", 8, 64, 8, 2000, 8, 64, W.BF16, 2.5)
+    small = _wl("small", 4, 32, 4, 700, 2, 64, W.BF16, 1.0)
+    dims_b, dims_s = _dims(td, big), _dims(td, small)
+    pb = td.new_plan_buffer(dims_b, DEV)
+    ids_b, _ = W.make_routing(big, seed=4)
+    run_plan(td, dims_b, ids_b, DEV, pb)
+    ids_s, _ = W.make_routing(small, seed=4)
+    lay = td.moonep_plan_layout(dims_s)
+    run_plan(td, dims_s, ids_s, DEV, pb[:lay.bytes])
+    g = read_plan(td, dims_s, pb[:lay.bytes])
+    assert_plan_equal(g, oracle.plan(small.R, small.E, small.K, small.S, small.B, ids_s))
+
+
+# ------------------------------------------------------------ full-size shapes
+
+@pytest.mark.parametrize("name", ["tiny", "uniform", "zipf", "k3", "decode"])
+def test_workload_plans_all_seeds(td, name):
+    wl = W.WORKLOADS[name]
+    dims = _dims(td, wl)
+    pb = td.new_plan_buffer(dims, DEV)
+    for seed in (0, 1, 2):
+        say(f"plan {name} seed {seed}")
+        ids, _ = W.make_routing(wl, seed)
+        run_plan(td, dims, ids, DEV, pb)
+        g = read_plan(td, dims, pb)
+        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+        assert_plan_equal(g, p)
+        if seed == 0:
+            check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g)
+        # every rank holds exactly S*K rows
+        assert np.all(g["seg_ptr"][np.arange(wl.R), wl.G + g["n_dup"]] == wl.SK)
+        say(f"  maxvio {float(g['maxvio'][0]):.3f}  dups/rank max {int(g['n_dup'].max())} "
+            f"(B={wl.B})  total dups {int(g['n_dup'].sum())}  status {int(g['status'][0])}")
+
+
+@pytest.mark.parametrize("name", ["uniform", "zipf", "k3", "decode"])
+def test_workload_data_moves_full_size(td, name):
+    wl = W.WORKLOADS[name]
+    dims = _dims(td, wl)
+    seed = 0
+    say(f"full-size moves {name}: {dims}")
+    ids, w = W.make_routing(wl, seed)
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+    pb, _ = run_plan(td, dims, ids, DEV)
+    assert_plan_equal(read_plan(td, dims, pb), p)
+    src_d = torch.from_numpy(p["src"].astype(np.int64)).to(DEV)
+    rng = np.random.default_rng(99)
+
+    # dispatch: every slot against the oracle's inverse map, windows through the oracle
+    hid = W.make_hidden(wl, seed, DEV)
+    recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hid.dtype, device=DEV)
+    say("  dispatch")
+    td.moonep_dispatch(dims, pb, hid, recv)
+    torch.cuda.synchronize()
+    hflat, rflat = hid.view(wl.n_tok, wl.H), recv.view(-1, wl.H)
+    for r in range(wl.R):
+        sl = slice(r * wl.SK, (r + 1) * wl.SK)
+        assert torch.equal(rflat[sl].view(torch.int16),
+                           hflat[src_d[sl] // wl.K].view(torch.int16)), f"dispatch rank {r}"
+    hid_h = bf16_bits(hid).reshape(wl.n_tok, wl.H)
+    for lo in list(rng.integers(0, wl.n_ent - 64, 6)) + [0, wl.n_ent - 64]:
+        want = oracle.dispatch(p, wl.K, hid_h, int(lo), int(lo) + 64)
+        assert np.array_equal(bf16_bits(rflat[int(lo):int(lo) + 64]), want)
+    del hid_h, hflat, hid
+
+    # combine: y = seeded expert outputs; sampled tokens through the oracle
+    say("  combine")
+    y = recv
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1234)
+    for r in range(wl.R):
+        y[r].copy_(torch.randn((wl.SK, wl.H), generator=g, device=DEV, dtype=torch.float32))
+    w_d = torch.from_numpy(w).to(DEV)
+    out = torch.empty((wl.R, wl.S, wl.H), dtype=torch.bfloat16, device=DEV)
+    td.moonep_combine(dims, pb, y, w_d, out)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([rng.integers(0, wl.n_tok, 300), [0, wl.n_tok - 1]]))
+    dsel = p["dst"].reshape(-1, wl.K)[toks].reshape(-1)
+    y_rows = bf16_bits(y.view(-1, wl.H)[torch.from_numpy(dsel.astype(np.int64)).to(DEV)])
+    want = oracle.combine(np.arange(dsel.size, dtype=np.int32), wl.K, y_rows,
+                          w.reshape(-1, wl.K)[toks].reshape(-1), W.BF16, W.BF16)
+    got = bf16_bits(out.view(wl.n_tok, wl.H)[torch.from_numpy(toks).to(DEV)])
+    assert np.array_equal(got, want), "combine"
+    del y, recv, out
+
+    # replicate: every materialised duplicate against the oracle's table
+    say("  replicate")
+    ew = W.make_expert_weights(wl, seed, DEV)
+    dup_w = torch.zeros((wl.R, wl.B) + tuple(wl.block_shape), dtype=ew.dtype, device=DEV)
+    td.moonep_replicate(dims, pb, ew, dup_w, wl.block_bytes)
+    torch.cuda.synchronize()
+    for r in range(wl.R):
+        for b in range(min(int(p["n_dup"][r]), wl.B)):
+            e = int(p["dup_expert"][r, b])
+            assert torch.equal(dup_w[r, b].view(torch.int16), ew[e].view(torch.int16))
+    del ew, dup_w
+
+    # reduce: sampled experts with duplicates through the oracle
+    say("  reduce")
+    dg, hg = W.make_grads(wl, seed, DEV)
+    n = wl.block_elems
+    nl = int(p["n_list"][0])
+    exps = sorted(set(p["list_expert"][:nl].tolist()))
+    pick = [exps[0], exps[-1]] + [exps[i] for i in rng.integers(0, len(exps), 3)]
+    pick = sorted(set(pick))
+    untouched = [e for e in range(wl.E) if e not in set(exps)][:3]
+    before = {e: hg[e].cpu().numpy() for e in pick + untouched}
+    td.moonep_reduce_dup_grads(dims, pb, dg, hg, n)
+    torch.cuda.synchronize()
+    for e in pick:
+        q0, q1 = int(p["dup_ptr"][e]), int(p["dup_ptr"][e + 1])
+        sel = [q for q in range(q0, q1) if p["list_b"][q] < wl.B]
+        dup_rows = np.stack([dg[int(p["list_rank"][q]), int(p["list_b"][q])].cpu().numpy()
+                             for q in sel]) if sel else np.zeros((0, n), np.float32)
+        sub = {"dup_ptr": np.array([0, len(sel)], np.int32),
+               "list_rank": np.zeros(len(sel), np.int32),
+               "list_b": np.arange(len(sel), dtype=np.int32)}
+        want = oracle.reduce_dup_grads(sub, len(sel), dup_rows.reshape(1, len(sel), n),
+                                       before[e].reshape(1, n))
+        assert np.array_equal(f32_bits(hg[e]), want.reshape(-1).view(np.uint32)), f"reduce e={e}"
+    for e in untouched:
+        assert np.array_equal(f32_bits(hg[e]), before[e].view(np.uint32)), f"expert {e} touched"
+    say(f"  ok ({len(pick)} experts reduced checked, {len(untouched)} untouched sampled)")

@@ -1,0 +1,216 @@
+"""Python binding of libmoonep.so: the balanced expert-parallel hot path on MI355X.
+
+Argument marshalling only. Every step of the plan, dispatch, replicate, combine
+and reduce runs in the HIP kernels of the library; torch provides device memory
+and streams. The functions carry the C names and take the same arguments:
+`dims` is a Dims, arrays are torch tensors on the GPU, `stream` is a
+torch.cuda.Stream (default: the current stream of the tensors' device).
+
+If the library has not been built this module raises ImportError: there is no
+other implementation to fall back on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoonep.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()' from the repository root)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32 = 0
+BF16 = 1
+STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
+
+ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_dispatch", "moonep_replicate",
+                "moonep_combine", "moonep_reduce_dup_grads", "moonep_strerror")
+
+
+class Dims(ctypes.Structure):
+    """moonep_dims: R ranks, E experts, K per token, S tokens per rank, B duplicate
+    slots per rank, dtype of hidden rows (F32/BF16), H hidden size."""
+    _fields_ = [("R", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("B", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("H", ctypes.c_int64)]
+
+    def __repr__(self):
+        return (f"Dims(R={self.R}, E={self.E}, K={self.K}, S={self.S}, B={self.B}, "
+                f"dtype={self.dtype}, H={self.H})")
+
+
+_LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D", "Opre",
+                   "Dpre", "dst", "src", "n_dup", "dup_expert", "dup_start", "dup_count",
+                   "seg_ptr", "seg_expert", "n_list", "list_expert", "list_rank", "list_b",
+                   "dup_ptr", "ws_tile_counts", "ws_tile_status", "ws_mat_pre", "ws_xlist",
+                   "ws_n_x")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = ([("bytes", ctypes.c_int64), ("dcap", ctypes.c_int32), ("pcap", ctypes.c_int32),
+                 ("n_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32)]
+                + [(n, ctypes.c_int64) for n in _LAYOUT_OFFSETS])
+
+
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_P_DIMS, _P_LAY = ctypes.POINTER(Dims), ctypes.POINTER(Layout)
+_lib.moonep_plan_layout.argtypes = [_P_DIMS, _P_LAY]
+_lib.moonep_plan.argtypes = [_P_DIMS, _vp, _vp, _vp]
+_lib.moonep_dispatch.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp]
+_lib.moonep_replicate.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
+_lib.moonep_combine.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp, _i32, _vp]
+_lib.moonep_reduce_dup_grads.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
+_lib.moonep_strerror.argtypes = [ctypes.c_int]
+_lib.moonep_strerror.restype = ctypes.c_char_p
+for _n in ENTRY_POINTS[:-1]:
+    getattr(_lib, _n).restype = ctypes.c_int
+
+
+class MoonEPError(RuntimeError):
+    def __init__(self, rc: int, where: str):
+        super().__init__(f"{where}: {moonep_strerror(rc)} (rc={rc})")
+        self.rc = rc
+
+
+def moonep_strerror(rc: int) -> str:
+    return _lib.moonep_strerror(rc).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise MoonEPError(rc, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, name: str, dtype=None, numel: Optional[int] = None) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() * t.element_size() < numel:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream, ref) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return stream.cuda_stream
+
+
+def _row_dtype(dims: Dims):
+    torch = _torch()
+    return torch.bfloat16 if dims.dtype == BF16 else torch.float32
+
+
+def moonep_plan_layout(dims: Dims) -> Layout:
+    lay = Layout()
+    _check(_lib.moonep_plan_layout(ctypes.byref(dims), ctypes.byref(lay)), "moonep_plan_layout")
+    return lay
+
+
+def moonep_plan(dims: Dims, topk_ids, plan_buf, stream=None) -> None:
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    ids = _ptr(topk_ids, "topk_ids", torch.int32, 4 * dims.R * dims.S * dims.K)
+    pb = _ptr(plan_buf, "plan_buf", None, lay.bytes)
+    _check(_lib.moonep_plan(ctypes.byref(dims), ids, pb, _stream(stream, plan_buf)), "moonep_plan")
+
+
+def moonep_dispatch(dims: Dims, plan_buf, hidden, recv, stream=None) -> None:
+    dt = _row_dtype(dims)
+    row = dims.H * (2 if dims.dtype == BF16 else 4)
+    lay = moonep_plan_layout(dims)
+    _check(_lib.moonep_dispatch(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(hidden, "hidden", dt, dims.R * dims.S * row),
+        _ptr(recv, "recv", dt, dims.R * dims.S * dims.K * row),
+        _stream(stream, recv)), "moonep_dispatch")
+
+
+def moonep_replicate(dims: Dims, plan_buf, expert_w, dup_w, block_bytes: int, stream=None) -> None:
+    lay = moonep_plan_layout(dims)
+    _check(_lib.moonep_replicate(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(expert_w, "expert_w", None, dims.E * block_bytes),
+        _ptr(dup_w, "dup_w", None, dims.R * dims.B * block_bytes),
+        int(block_bytes), _stream(stream, dup_w)), "moonep_replicate")
+
+
+def moonep_combine(dims: Dims, plan_buf, y, topk_w, out, out_dtype: Optional[int] = None,
+                   stream=None) -> None:
+    torch = _torch()
+    od = dims.dtype if out_dtype is None else int(out_dtype)
+    row = dims.H * (2 if dims.dtype == BF16 else 4)
+    orow = dims.H * (2 if od == BF16 else 4)
+    lay = moonep_plan_layout(dims)
+    _check(_lib.moonep_combine(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(y, "y", _row_dtype(dims), dims.R * dims.S * dims.K * row),
+        _ptr(topk_w, "topk_w", torch.float32, 4 * dims.R * dims.S * dims.K),
+        _ptr(out, "out", torch.bfloat16 if od == BF16 else torch.float32, dims.R * dims.S * orow),
+        od, _stream(stream, out)), "moonep_combine")
+
+
+def moonep_reduce_dup_grads(dims: Dims, plan_buf, dup_grads, home_grads, block_elems: int,
+                            stream=None) -> None:
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    _check(_lib.moonep_reduce_dup_grads(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(dup_grads, "dup_grads", torch.float32, 4 * dims.R * dims.B * block_elems),
+        _ptr(home_grads, "home_grads", torch.float32, 4 * dims.E * block_elems),
+        int(block_elems), _stream(stream, home_grads)), "moonep_reduce_dup_grads")
+
+
+# ------------------------------------------------------------- buffer helpers
+
+def dims_of(R: int, E: int, K: int, S: int, B: int, H: int, dtype: int) -> Dims:
+    return Dims(R, E, K, S, B, dtype, H)
+
+
+def new_plan_buffer(dims: Dims, device="cuda"):
+    """A device buffer of the size the plan layout asks for."""
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    return torch.empty(lay.bytes, dtype=torch.uint8, device=device)
+
+
+def plan_views(dims: Dims, plan_buf) -> Dict[str, "torch.Tensor"]:
+    """Typed views of the public plan arrays inside plan_buf (no copies)."""
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    R, E, S, K = dims.R, dims.E, dims.S, dims.K
+    G, NE, dcap, pcap = E // R, R * S * K, lay.dcap, lay.pcap
+    shapes = {
+        "status": (1,), "maxT": (1,), "T": (E,), "hoff": (E,), "L": (R,), "keep": (R,),
+        "O": (R,), "D": (R,), "Opre": (R + 1,), "Dpre": (R + 1,), "dst": (NE,), "src": (NE,),
+        "n_dup": (R,), "dup_expert": (R, dcap), "dup_start": (R, dcap), "dup_count": (R, dcap),
+        "seg_ptr": (R, G + dcap + 1), "seg_expert": (R, G + dcap), "n_list": (1,),
+        "list_expert": (pcap,), "list_rank": (pcap,), "list_b": (pcap,), "dup_ptr": (E + 1,),
+    }
+    out = {}
+    for name, shp in shapes.items():
+        off = getattr(lay, name)
+        n = 1
+        for s in shp:
+            n *= s
+        out[name] = plan_buf[off:off + 4 * n].view(torch.int32).view(shp)
+    out["maxvio"] = plan_buf[lay.maxvio:lay.maxvio + 8].view(torch.float64)
+    return out

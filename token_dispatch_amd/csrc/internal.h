@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel
+// translation units (plan.hip, move.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moonep.h"
+
+namespace moonep {
+
+// Hard limits of the kernels (checked by the ABI layer before any launch).
+constexpr int kMaxE = 1024;        // LDS histogram bins of the plan kernels
+constexpr int kMaxR = 1024;        // one rank per thread in the solve kernel
+constexpr int kMaxK = 64;          // one entry of a token per lane
+constexpr int kTileEntries = 4096; // entries per plan tile (rounded down to whole tokens)
+constexpr int kPlanThreads = 256;  // count / assign workgroup
+constexpr int kSolveThreads = 1024;
+
+// Typed device pointers into one plan buffer, resolved from the byte layout.
+struct PlanPtrs {
+    int32_t *status, *maxT;
+    double *maxvio;
+    int32_t *T, *hoff, *L, *keep, *O, *D, *Opre, *Dpre, *dst, *src;
+    int32_t *n_dup, *dup_expert, *dup_start, *dup_count, *seg_ptr, *seg_expert;
+    int32_t *n_list, *list_expert, *list_rank, *list_b, *dup_ptr;
+    int32_t *tile_counts, *tile_status, *mat_pre, *xlist, *n_x;
+};
+
+// Shape constants every kernel needs, computed once on the host.
+struct PlanShape {
+    int32_t R, E, K, S, B, G;
+    int32_t SK;           // rows per rank
+    int32_t n_tok;        // R*S
+    int32_t n_ent;        // R*S*K
+    int32_t dcap, pcap;
+    int32_t n_tiles, tile_tokens;
+    int32_t id_bits;      // bits needed to tell expert ids apart (ceil log2 E, >= 1)
+};
+
+PlanPtrs resolve(const moonep_layout &lay, void *base);
+
+hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p,
+                       hipStream_t st);
+
+hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *hidden,
+                           void *recv, int64_t row_bytes, hipStream_t st);
+
+hipError_t launch_combine(const PlanShape &sh, const PlanPtrs &p, const void *y,
+                          const float *w, void *out, int in_bf16, int out_bf16, int64_t H,
+                          hipStream_t st);
+
+hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *expert_w,
+                            void *dup_w, int64_t block_bytes, hipStream_t st);
+
+hipError_t launch_reduce(const PlanShape &sh, const PlanPtrs &p, const float *dup_grads,
+                         float *home_grads, int64_t block_elems, hipStream_t st);
+
+}  // namespace moonep

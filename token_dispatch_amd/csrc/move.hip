@@ -1,0 +1,375 @@
+// Data-move kernels for gfx950 driven by a plan: dispatch, combine, replicate
+// and the duplicate-gradient reduce. All four are HBM-bound row moves: rows are
+// moved as 16-byte vectors, one wave covers 64 x 16 B = 1 KiB per instruction,
+// so every global access is a fully coalesced, 1 KiB-aligned-in-row burst.
+//
+// dispatch  tokens are written straight into the static expert-grouped buffer
+//           (news.hamidun.com EN, "Why this matters to engineers"): one wave per
+//           (token, row segment) reads the segment once into registers and
+//           stores it to the token's K slots. Stores are non-temporal: the
+//           receive buffer is far larger than L2 and the MALL and is not re-read
+//           by this kernel.
+// combine   the weighted sum of a token's K expert outputs: one wave per
+//           (token, row segment), binary32 fma in ascending k, one store.
+// replicate duplicate experts are fetched from home before compute ("How MoonEP
+//           works", same page): a fixed grid walks (duplicate slot, block piece).
+// reduce    duplicate gradients back to home ("How MoonEP works"): a fixed grid
+//           walks (expert with duplicates, block piece); each element is summed
+//           home first, then duplicates in ascending rank.
+#include "internal.h"
+
+namespace moonep {
+namespace {
+
+// Native 16-byte vector: what global_load/store_dwordx4 move, and what the
+// non-temporal store builtin accepts.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kMoveThreads = 256;
+constexpr int kMoveWaves = kMoveThreads / 64;
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Round binary32 to bf16, nearest-even; NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- dispatch
+// Work item = (token, segment of 64*CPL chunks). C = 16-byte chunks per row.
+template <int CPL>
+__global__ __launch_bounds__(kMoveThreads) void k_dispatch(const v4u *__restrict__ hidden,
+                                                           v4u *__restrict__ recv,
+                                                           const int32_t *__restrict__ dst,
+                                                           int64_t n_items, int32_t segs,
+                                                           int32_t C, int32_t K,
+                                                           int64_t n_slots) {
+    const int lane = lane_id();
+    const int64_t item = (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int64_t tok = item / segs;
+    const int seg = (int)(item - tok * segs);
+    const int cbase = seg * 64 * CPL + lane;
+    const int my_dst = lane < K ? dst[tok * K + lane] : -1;
+
+    v4u v[CPL];
+    const v4u *row = hidden + tok * C;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = cbase + i * 64;
+        if (c < C) v[i] = row[c];
+    }
+    for (int k = 0; k < K; ++k) {
+        const int d = readlane_i(my_dst, k);
+        if (d < 0 || d >= n_slots) continue;
+        v4u *out = recv + (int64_t)d * C;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = cbase + i * 64;
+            if (c < C) __builtin_nontemporal_store(v[i], out + c);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- combine
+template <bool IN_BF16>
+struct Chunk;
+template <>
+struct Chunk<true> {  // 8 bf16
+    static constexpr int N = 8;
+    __device__ static void unpack(const v4u &q, float *x) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(w[j] << 16);
+            x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+};
+template <>
+struct Chunk<false> {  // 4 f32
+    static constexpr int N = 4;
+    __device__ static void unpack(const v4u &q, float *x) {
+        x[0] = __uint_as_float(q.x);
+        x[1] = __uint_as_float(q.y);
+        x[2] = __uint_as_float(q.z);
+        x[3] = __uint_as_float(q.w);
+    }
+};
+
+template <int N, bool OUT_BF16>
+__device__ __forceinline__ void store_elems(void *out, int64_t elem0, const float *a) {
+    if constexpr (OUT_BF16) {
+        uint32_t w[N / 2];
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) w[j] = bf16_rne(a[2 * j]) | (bf16_rne(a[2 * j + 1]) << 16);
+        uint16_t *o = reinterpret_cast<uint16_t *>(out) + elem0;
+        if constexpr (N == 8) {
+            *reinterpret_cast<v4u *>(o) = v4u{w[0], w[1], w[2], w[3]};
+        } else {
+            *reinterpret_cast<uint2 *>(o) = make_uint2(w[0], w[1]);
+        }
+    } else {
+        float *o = reinterpret_cast<float *>(out) + elem0;
+#pragma unroll
+        for (int j = 0; j < N; j += 4)
+            *reinterpret_cast<float4 *>(o + j) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
+    }
+}
+
+template <int CPL, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict__ y,
+                                                          const float *__restrict__ w,
+                                                          const int32_t *__restrict__ dst,
+                                                          void *__restrict__ out,
+                                                          int64_t n_items, int32_t segs,
+                                                          int32_t C, int32_t K,
+                                                          int64_t n_slots) {
+    using Ch = Chunk<IN_BF16>;
+    constexpr int N = Ch::N;
+    const int lane = lane_id();
+    const int64_t item = (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int64_t tok = item / segs;
+    const int seg = (int)(item - tok * segs);
+    const int cbase = seg * 64 * CPL + lane;
+    const int my_dst = lane < K ? dst[tok * K + lane] : -1;
+    const float my_w = lane < K ? w[tok * K + lane] : 0.0f;
+
+    float acc[CPL][N];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int j = 0; j < N; ++j) acc[i][j] = 0.0f;
+
+    for (int k = 0; k < K; ++k) {
+        const int d = readlane_i(my_dst, k);
+        const float wk = readlane_f(my_w, k);
+        if (d < 0 || d >= n_slots) continue;
+        const v4u *row = y + (int64_t)d * C;
+        v4u v[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = cbase + i * 64;
+            v[i] = c < C ? row[c] : v4u{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            float x[N];
+            Ch::unpack(v[i], x);
+#pragma unroll
+            for (int j = 0; j < N; ++j) acc[i][j] = __builtin_fmaf(wk, x[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = cbase + i * 64;
+        if (c < C) store_elems<N, OUT_BF16>(out, (tok * C + c) * N, acc[i]);
+    }
+}
+
+// ---------------------------------------------------------------- replicate
+constexpr int kCopyUnroll = 8;                         // 16-byte chunks per thread per item
+constexpr int kCopyChunks = kMoveThreads * kCopyUnroll;  // 32 KiB per work item
+
+__global__ __launch_bounds__(kMoveThreads) void k_replicate(
+    const v4u *__restrict__ expert_w, v4u *__restrict__ dup_w,
+    const int32_t *__restrict__ mat_pre, const int32_t *__restrict__ dup_expert, int32_t R,
+    int32_t E, int32_t B, int32_t dcap, int64_t block_chunks, int64_t items_per_slot) {
+    const int64_t total = (int64_t)mat_pre[R] * items_per_slot;
+    for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
+        const int64_t q = item / items_per_slot;
+        const int64_t part = item - q * items_per_slot;
+        int lo = 0, hi = R + 1;  // rank r with mat_pre[r] <= q < mat_pre[r+1]
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (mat_pre[mid] <= q) lo = mid + 1; else hi = mid;
+        }
+        const int r = lo - 1;
+        const int b = (int)(q - mat_pre[r]);
+        const int e = dup_expert[(int64_t)r * dcap + b];
+        if (e < 0 || e >= E) continue;  // only a broken plan gets here
+        const v4u *s = expert_w + (int64_t)e * block_chunks;
+        v4u *d = dup_w + ((int64_t)r * B + b) * block_chunks;
+        const int64_t c0 = part * kCopyChunks + threadIdx.x;
+        v4u v[kCopyUnroll];
+#pragma unroll
+        for (int i = 0; i < kCopyUnroll; ++i) {
+            const int64_t c = c0 + (int64_t)i * kMoveThreads;
+            if (c < block_chunks) v[i] = s[c];
+        }
+#pragma unroll
+        for (int i = 0; i < kCopyUnroll; ++i) {
+            const int64_t c = c0 + (int64_t)i * kMoveThreads;
+            if (c < block_chunks) __builtin_nontemporal_store(v[i], d + c);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- reduce
+constexpr int kRedUnroll = 4;
+constexpr int kRedVecs = kMoveThreads * kRedUnroll;  // float4 per work item
+
+__global__ __launch_bounds__(kMoveThreads) void k_reduce(
+    const float4 *__restrict__ dup_grads, float4 *__restrict__ home,
+    const int32_t *__restrict__ xlist, const int32_t *__restrict__ n_x,
+    const int32_t *__restrict__ dup_ptr, const int32_t *__restrict__ list_rank,
+    const int32_t *__restrict__ list_b, int32_t R, int32_t B, int64_t n4,
+    int64_t items_per_expert) {
+    const int64_t total = (int64_t)n_x[0] * items_per_expert;
+    for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
+        const int64_t xi = item / items_per_expert;
+        const int64_t part = item - xi * items_per_expert;
+        const int e = xlist[xi];
+        const int p0 = dup_ptr[e], p1 = dup_ptr[e + 1];
+        bool any = false;
+        for (int q = p0; q < p1; ++q) any |= list_b[q] < B;
+        if (!any) continue;
+        float4 *h = home + (int64_t)e * n4;
+        const int64_t j0 = part * kRedVecs + threadIdx.x;
+        float4 acc[kRedUnroll];
+#pragma unroll
+        for (int i = 0; i < kRedUnroll; ++i) {
+            const int64_t j = j0 + (int64_t)i * kMoveThreads;
+            if (j < n4) acc[i] = h[j];
+        }
+        for (int q = p0; q < p1; ++q) {
+            const int b = list_b[q], rk = list_rank[q];
+            if (b < 0 || b >= B || rk < 0 || rk >= R) continue;
+            const float4 *g = dup_grads + ((int64_t)rk * B + b) * n4;
+#pragma unroll
+            for (int i = 0; i < kRedUnroll; ++i) {
+                const int64_t j = j0 + (int64_t)i * kMoveThreads;
+                if (j < n4) {
+                    const float4 t = g[j];
+                    acc[i].x = acc[i].x + t.x;
+                    acc[i].y = acc[i].y + t.y;
+                    acc[i].z = acc[i].z + t.z;
+                    acc[i].w = acc[i].w + t.w;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRedUnroll; ++i) {
+            const int64_t j = j0 + (int64_t)i * kMoveThreads;
+            if (j < n4) h[j] = acc[i];
+        }
+    }
+}
+
+// Chunks per lane of one row segment: the row is split into the fewest segments
+// of at most 16 chunks per lane, then each segment takes an instantiated width.
+int pick_cpl(int64_t C) {
+    const int64_t per_lane = (C + 63) / 64;
+    const int64_t segs = (per_lane + 15) / 16;
+    const int64_t need = (per_lane + segs - 1) / segs;
+    static const int widths[] = {1, 2, 4, 7, 8, 14, 16};
+    for (int w : widths)
+        if (w >= need) return w;
+    return 16;
+}
+
+// Grid of the fixed-size copy kernels: enough workgroups to fill 256 CUs.
+constexpr int kCopyGrid = 256 * 8;
+
+}  // namespace
+
+hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *hidden,
+                           void *recv, int64_t row_bytes, hipStream_t st) {
+    const int64_t C = row_bytes / 16;
+    const int cpl = pick_cpl(C);
+    const int32_t segs = (int32_t)((C + 64 * cpl - 1) / (64 * cpl));
+    const int64_t items = (int64_t)sh.n_tok * segs;
+    const dim3 grid((unsigned)((items + kMoveWaves - 1) / kMoveWaves));
+    const int64_t n_slots = (int64_t)sh.n_ent;
+    auto h = static_cast<const v4u *>(hidden);
+    auto r = static_cast<v4u *>(recv);
+#define MOONEP_DISPATCH(W)                                                                  \
+    case W:                                                                                 \
+        hipLaunchKernelGGL(k_dispatch<W>, grid, dim3(kMoveThreads), 0, st, h, r, p.dst,   \
+                           items, segs, (int32_t)C, sh.K, n_slots);                         \
+        break;
+    switch (cpl) {
+        MOONEP_DISPATCH(1)
+        MOONEP_DISPATCH(2)
+        MOONEP_DISPATCH(4)
+        MOONEP_DISPATCH(7)
+        MOONEP_DISPATCH(8)
+        MOONEP_DISPATCH(14)
+        MOONEP_DISPATCH(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef MOONEP_DISPATCH
+    return hipGetLastError();
+}
+
+template <bool IB, bool OB>
+static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const void *y,
+                                const float *w, void *out, int64_t C, hipStream_t st) {
+    const int cpl = pick_cpl(C);
+    const int32_t segs = (int32_t)((C + 64 * cpl - 1) / (64 * cpl));
+    const int64_t items = (int64_t)sh.n_tok * segs;
+    const dim3 grid((unsigned)((items + kMoveWaves - 1) / kMoveWaves));
+    const int64_t n_slots = (int64_t)sh.n_ent;
+    auto yy = static_cast<const v4u *>(y);
+#define MOONEP_COMBINE(W)                                                                 \
+    case W:                                                                               \
+        hipLaunchKernelGGL((k_combine<W, IB, OB>), grid, dim3(kMoveThreads), 0, st, yy, w, \
+                           p.dst, out, items, segs, (int32_t)C, sh.K, n_slots);           \
+        break;
+    switch (cpl) {
+        MOONEP_COMBINE(1)
+        MOONEP_COMBINE(2)
+        MOONEP_COMBINE(4)
+        MOONEP_COMBINE(7)
+        MOONEP_COMBINE(8)
+        MOONEP_COMBINE(14)
+        MOONEP_COMBINE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef MOONEP_COMBINE
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const PlanShape &sh, const PlanPtrs &p, const void *y,
+                          const float *w, void *out, int in_bf16, int out_bf16, int64_t H,
+                          hipStream_t st) {
+    const int64_t C = H * (in_bf16 ? 2 : 4) / 16;
+    if (in_bf16 && out_bf16) return combine_typed<true, true>(sh, p, y, w, out, C, st);
+    if (in_bf16) return combine_typed<true, false>(sh, p, y, w, out, C, st);
+    if (out_bf16) return combine_typed<false, true>(sh, p, y, w, out, C, st);
+    return combine_typed<false, false>(sh, p, y, w, out, C, st);
+}
+
+hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *expert_w,
+                            void *dup_w, int64_t block_bytes, hipStream_t st) {
+    if (sh.B == 0) return hipSuccess;
+    const int64_t chunks = block_bytes / 16;
+    const int64_t ips = (chunks + kCopyChunks - 1) / kCopyChunks;
+    hipLaunchKernelGGL(k_replicate, dim3(kCopyGrid), dim3(kMoveThreads), 0, st,
+                       static_cast<const v4u *>(expert_w), static_cast<v4u *>(dup_w),
+                       p.mat_pre, p.dup_expert, sh.R, sh.E, sh.B, sh.dcap, chunks, ips);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const PlanShape &sh, const PlanPtrs &p, const float *dup_grads,
+                         float *home_grads, int64_t block_elems, hipStream_t st) {
+    if (sh.B == 0) return hipSuccess;
+    const int64_t n4 = block_elems / 4;
+    const int64_t ipe = (n4 + kRedVecs - 1) / kRedVecs;
+    hipLaunchKernelGGL(k_reduce, dim3(kCopyGrid), dim3(kMoveThreads), 0, st,
+                       reinterpret_cast<const float4 *>(dup_grads),
+                       reinterpret_cast<float4 *>(home_grads), p.xlist, p.n_x, p.dup_ptr,
+                       p.list_rank, p.list_b, sh.R, sh.B, n4, ipe);
+    return hipGetLastError();
+}
+
+}  // namespace moonep
