@@ -244,6 +244,7 @@ def main():
         "op_gbs": {k: round(x, 1) for k, x in gbs.items()},
         "maxvio_before": round(maxvio, 4), "rank_maxvio_after": rank_maxvio_after,
         "dups_per_rank_max": int(n_dup.max()), "dups_total": int(n_dup.sum()), "B": wl.B,
+        "dups_materialised": n_mat, "experts_with_dups": n_xm,
         "status": status, "kernel_source_hash": src_hash,
         "roofline": roofline, "cpu_baseline": cpu,
     }
