@@ -3,14 +3,24 @@
 // moved as 16-byte vectors, one wave covers 64 x 16 B = 1 KiB per instruction,
 // so every global access is a fully coalesced, 1 KiB-aligned-in-row burst.
 //
+// Read/write phasing. On MI355X a stream of reads with a few percent of writes
+// mixed in (or the reverse) runs far below either pure stream: the memory side
+// pays for every switch of direction, whichever CUs or XCDs issue the minority
+// traffic. Dispatch (94% writes) and combine (94% reads) therefore run as a
+// short sequence of launches over token chunks, so the minority traffic of a
+// chunk arrives in one burst instead of being spread over the whole kernel:
+//
 // dispatch  tokens are written straight into the static expert-grouped buffer
-//           (news.hamidun.com EN, "Why this matters to engineers"): one wave per
-//           (token, row segment) reads the segment once into registers and
-//           stores it to the token's K slots. Stores are non-temporal: the
-//           receive buffer is far larger than L2 and the MALL and is not re-read
-//           by this kernel.
+//           (news.hamidun.com EN, "Why this matters to engineers"). Each launch
+//           is one resident grid; every wave first loads TPW row segments
+//           (non-temporal: each is read once) into registers, then stores each
+//           to the token's K slots. The reads of a chunk thus all happen at the
+//           start of its launch and the rest of the launch only writes.
 // combine   the weighted sum of a token's K expert outputs: one wave per
-//           (token, row segment), binary32 fma in ascending k, one store.
+//           (token, row segment), binary32 fma in ascending k, one store; a
+//           launch covers a chunk of tokens whose output is a few tens of MB.
+//           Loads and stores are non-temporal (the expert outputs are read once,
+//           the result is not re-read by this kernel).
 // replicate duplicate experts are fetched from home before compute ("How MoonEP
 //           works", same page): a fixed grid walks (duplicate slot, block piece).
 // reduce    duplicate gradients back to home ("How MoonEP works"): a fixed grid
@@ -45,36 +55,49 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // ---------------------------------------------------------------- dispatch
 // Work item = (token, segment of 64*CPL chunks). C = 16-byte chunks per row.
-template <int CPL>
+// One launch covers items [i_lo, i_hi); wave w of the grid takes items
+// i_lo + t * n_waves + w for t < TPW, loads all of them, then stores them.
+template <int CPL, int TPW>
 __global__ __launch_bounds__(kMoveThreads) void k_dispatch(const v4u *__restrict__ hidden,
                                                            v4u *__restrict__ recv,
                                                            const int32_t *__restrict__ dst,
-                                                           int64_t n_items, int32_t segs,
-                                                           int32_t C, int32_t K,
+                                                           int64_t i_lo, int64_t i_hi,
+                                                           int32_t segs, int32_t C, int32_t K,
                                                            int64_t n_slots) {
     const int lane = lane_id();
-    const int64_t item = (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
-    if (item >= n_items) return;
-    const int64_t tok = item / segs;
-    const int seg = (int)(item - tok * segs);
-    const int cbase = seg * 64 * CPL + lane;
-    const int my_dst = lane < K ? dst[tok * K + lane] : -1;
-
-    v4u v[CPL];
-    const v4u *row = hidden + tok * C;
+    const int64_t n_waves = (int64_t)gridDim.x * kMoveWaves;
+    const int64_t wave = (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
+    v4u v[TPW][CPL];
+    int my_dst[TPW], cbase[TPW];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = cbase + i * 64;
-        if (c < C) v[i] = row[c];
+    for (int t = 0; t < TPW; ++t) {
+        const int64_t item = i_lo + t * n_waves + wave;
+        my_dst[t] = -1;
+        cbase[t] = C;  // no chunk of an absent item passes the c < C tests
+        if (item < i_hi) {
+            const int64_t tok = item / segs;
+            const int seg = (int)(item - tok * segs);
+            cbase[t] = seg * 64 * CPL + lane;
+            if (lane < K) my_dst[t] = dst[tok * K + lane];
+            const v4u *row = hidden + tok * C;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = cbase[t] + i * 64;
+                if (c < C) v[t][i] = __builtin_nontemporal_load(row + c);
+            }
+        }
     }
-    for (int k = 0; k < K; ++k) {
-        const int d = readlane_i(my_dst, k);
-        if (d < 0 || d >= n_slots) continue;
-        v4u *out = recv + (int64_t)d * C;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = cbase + i * 64;
-            if (c < C) __builtin_nontemporal_store(v[i], out + c);
+    for (int t = 0; t < TPW; ++t) {
+        for (int k = 0; k < K; ++k) {
+            const int d = readlane_i(my_dst[t], k);
+            if (d < 0 || d >= n_slots) continue;
+            v4u *out = recv + (int64_t)d * C;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = cbase[t] + i * 64;
+                if (c < C) out[c] = v[t][i];
+            }
         }
     }
 }
@@ -105,6 +128,10 @@ struct Chunk<false> {  // 4 f32
     }
 };
 
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Store N accumulators (elements elem0 .. elem0+N-1 of out) non-temporally.
 template <int N, bool OUT_BF16>
 __device__ __forceinline__ void store_elems(void *out, int64_t elem0, const float *a) {
     if constexpr (OUT_BF16) {
@@ -113,31 +140,33 @@ __device__ __forceinline__ void store_elems(void *out, int64_t elem0, const floa
         for (int j = 0; j < N / 2; ++j) w[j] = bf16_rne(a[2 * j]) | (bf16_rne(a[2 * j + 1]) << 16);
         uint16_t *o = reinterpret_cast<uint16_t *>(out) + elem0;
         if constexpr (N == 8) {
-            *reinterpret_cast<v4u *>(o) = v4u{w[0], w[1], w[2], w[3]};
+            __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u *>(o));
         } else {
-            *reinterpret_cast<uint2 *>(o) = make_uint2(w[0], w[1]);
+            __builtin_nontemporal_store(v2u{w[0], w[1]}, reinterpret_cast<v2u *>(o));
         }
     } else {
         float *o = reinterpret_cast<float *>(out) + elem0;
 #pragma unroll
         for (int j = 0; j < N; j += 4)
-            *reinterpret_cast<float4 *>(o + j) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
+            __builtin_nontemporal_store(v4f{a[j], a[j + 1], a[j + 2], a[j + 3]},
+                                        reinterpret_cast<v4f *>(o + j));
     }
 }
 
+// One wave per work item (token, row segment) of the launch's range [i_lo, i_hi).
 template <int CPL, bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict__ y,
                                                           const float *__restrict__ w,
                                                           const int32_t *__restrict__ dst,
                                                           void *__restrict__ out,
-                                                          int64_t n_items, int32_t segs,
-                                                          int32_t C, int32_t K,
+                                                          int64_t i_lo, int64_t i_hi,
+                                                          int32_t segs, int32_t C, int32_t K,
                                                           int64_t n_slots) {
     using Ch = Chunk<IN_BF16>;
     constexpr int N = Ch::N;
     const int lane = lane_id();
-    const int64_t item = (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
-    if (item >= n_items) return;
+    const int64_t item = i_lo + (int64_t)blockIdx.x * kMoveWaves + (threadIdx.x >> 6);
+    if (item >= i_hi) return;
     const int64_t tok = item / segs;
     const int seg = (int)(item - tok * segs);
     const int cbase = seg * 64 * CPL + lane;
@@ -159,7 +188,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict_
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = cbase + i * 64;
-            v[i] = c < C ? row[c] : v4u{0u, 0u, 0u, 0u};
+            v[i] = c < C ? __builtin_nontemporal_load(row + c) : v4u{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -282,49 +311,106 @@ constexpr int kCopyGrid = 256 * 8;
 
 }  // namespace
 
+// Row segments of a dispatch wave, by chunks per lane: as many as fit in about
+// 200 VGPRs of row data, which keeps two waves per SIMD resident.
+constexpr int tpw_of(int cpl) { return cpl >= 14 ? 3 : cpl >= 8 ? 6 : cpl >= 7 ? 7 : 8; }
+
+// Workgroups of k_dispatch<CPL, TPW> that the current device holds at once.
+template <int CPL>
+int resident_dispatch_wgs() {
+    static int cached[64];  // per device; 0 = not yet queried (benign race: same value)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_dispatch<CPL, tpw_of(CPL)>,
+                                                     kMoveThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    v = cus * per_cu;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+    return v;
+}
+
+template <int CPL>
+hipError_t dispatch_chunks(const v4u *h, v4u *r, const int32_t *dst, int64_t items, int32_t segs,
+                           int32_t C, int32_t K, int64_t n_slots, hipStream_t st) {
+    constexpr int TPW = tpw_of(CPL);
+    const int64_t full = resident_dispatch_wgs<CPL>();
+    const int64_t per_launch = full * kMoveWaves * TPW;
+    for (int64_t lo = 0; lo < items; lo += per_launch) {
+        const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
+        // the last launch only needs enough waves for what is left
+        const int64_t waves = (hi - lo + TPW - 1) / TPW;
+        const int64_t wgs = (waves + kMoveWaves - 1) / kMoveWaves;
+        hipLaunchKernelGGL((k_dispatch<CPL, TPW>), dim3((unsigned)(wgs < full ? wgs : full)),
+                           dim3(kMoveThreads), 0, st, h, r, dst, lo, hi, segs, C, K, n_slots);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *hidden,
                            void *recv, int64_t row_bytes, hipStream_t st) {
     const int64_t C = row_bytes / 16;
     const int cpl = pick_cpl(C);
     const int32_t segs = (int32_t)((C + 64 * cpl - 1) / (64 * cpl));
     const int64_t items = (int64_t)sh.n_tok * segs;
-    const dim3 grid((unsigned)((items + kMoveWaves - 1) / kMoveWaves));
     const int64_t n_slots = (int64_t)sh.n_ent;
     auto h = static_cast<const v4u *>(hidden);
     auto r = static_cast<v4u *>(recv);
-#define MOONEP_DISPATCH(W)                                                                  \
-    case W:                                                                                 \
-        hipLaunchKernelGGL(k_dispatch<W>, grid, dim3(kMoveThreads), 0, st, h, r, p.dst,   \
-                           items, segs, (int32_t)C, sh.K, n_slots);                         \
-        break;
     switch (cpl) {
-        MOONEP_DISPATCH(1)
-        MOONEP_DISPATCH(2)
-        MOONEP_DISPATCH(4)
-        MOONEP_DISPATCH(7)
-        MOONEP_DISPATCH(8)
-        MOONEP_DISPATCH(14)
-        MOONEP_DISPATCH(16)
+        case 1: return dispatch_chunks<1>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 2: return dispatch_chunks<2>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 4: return dispatch_chunks<4>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 7: return dispatch_chunks<7>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 8: return dispatch_chunks<8>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 14: return dispatch_chunks<14>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
+        case 16: return dispatch_chunks<16>(h, r, p.dst, items, segs, (int32_t)C, sh.K, n_slots, st);
         default: return hipErrorInvalidValue;
     }
-#undef MOONEP_DISPATCH
-    return hipGetLastError();
+}
+
+// Output bytes one combine launch writes (about): large enough that launch gaps
+// stay small, small enough that the chunk's stores come as one burst.
+constexpr int64_t kCombineChunkOutBytes = 56ll << 20;
+
+template <int CPL, bool IB, bool OB>
+hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void *out,
+                          int64_t n_tok, int32_t segs, int32_t C, int32_t K, int64_t n_slots,
+                          int64_t out_row_bytes, hipStream_t st) {
+    int64_t tok_per = kCombineChunkOutBytes / out_row_bytes;
+    if (tok_per < 64) tok_per = 64;
+    const int64_t per_launch = tok_per * segs;
+    const int64_t items = n_tok * segs;
+    for (int64_t lo = 0; lo < items; lo += per_launch) {
+        const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
+        const dim3 grid((unsigned)((hi - lo + kMoveWaves - 1) / kMoveWaves));
+        hipLaunchKernelGGL((k_combine<CPL, IB, OB>), grid, dim3(kMoveThreads), 0, st, y, w, dst,
+                           out, lo, hi, segs, C, K, n_slots);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <bool IB, bool OB>
 static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const void *y,
-                                const float *w, void *out, int64_t C, hipStream_t st) {
+                                const float *w, void *out, int64_t C, int64_t H, hipStream_t st) {
     const int cpl = pick_cpl(C);
     const int32_t segs = (int32_t)((C + 64 * cpl - 1) / (64 * cpl));
-    const int64_t items = (int64_t)sh.n_tok * segs;
-    const dim3 grid((unsigned)((items + kMoveWaves - 1) / kMoveWaves));
     const int64_t n_slots = (int64_t)sh.n_ent;
+    const int64_t orow = H * (OB ? 2 : 4);
     auto yy = static_cast<const v4u *>(y);
-#define MOONEP_COMBINE(W)                                                                 \
-    case W:                                                                               \
-        hipLaunchKernelGGL((k_combine<W, IB, OB>), grid, dim3(kMoveThreads), 0, st, yy, w, \
-                           p.dst, out, items, segs, (int32_t)C, sh.K, n_slots);           \
-        break;
+#define MOONEP_COMBINE(W)                                                                  \
+    case W:                                                                                \
+        return combine_chunks<W, IB, OB>(yy, w, p.dst, out, sh.n_tok, segs, (int32_t)C, sh.K, \
+                                         n_slots, orow, st);
     switch (cpl) {
         MOONEP_COMBINE(1)
         MOONEP_COMBINE(2)
@@ -336,17 +422,16 @@ static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const vo
         default: return hipErrorInvalidValue;
     }
 #undef MOONEP_COMBINE
-    return hipGetLastError();
 }
 
 hipError_t launch_combine(const PlanShape &sh, const PlanPtrs &p, const void *y,
                           const float *w, void *out, int in_bf16, int out_bf16, int64_t H,
                           hipStream_t st) {
     const int64_t C = H * (in_bf16 ? 2 : 4) / 16;
-    if (in_bf16 && out_bf16) return combine_typed<true, true>(sh, p, y, w, out, C, st);
-    if (in_bf16) return combine_typed<true, false>(sh, p, y, w, out, C, st);
-    if (out_bf16) return combine_typed<false, true>(sh, p, y, w, out, C, st);
-    return combine_typed<false, false>(sh, p, y, w, out, C, st);
+    if (in_bf16 && out_bf16) return combine_typed<true, true>(sh, p, y, w, out, C, H, st);
+    if (in_bf16) return combine_typed<true, false>(sh, p, y, w, out, C, H, st);
+    if (out_bf16) return combine_typed<false, true>(sh, p, y, w, out, C, H, st);
+    return combine_typed<false, false>(sh, p, y, w, out, C, H, st);
 }
 
 hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *expert_w,
