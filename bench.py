@@ -48,18 +48,68 @@ def algorithmic_bytes(wl, n_mat, n_xm):
     return {"dispatch": d, "combine": c, "replicate": rep, "reduce": red, "plan": plan}
 
 
-def traffic_for(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
-    if not os.path.exists(path):
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
+
+# Library kernels behind each C-ABI call (one call may enqueue several launches).
+OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_assign"), "replicate": ("k_replicate",),
+              "dispatch": ("k_dispatch",), "combine": ("k_combine",), "reduce": ("k_reduce",)}
+COPY_CAL_BYTES = 1 << 30
+
+
+def traffic_for(op: str, src_hash: str):
+    """HBM bytes per call of `op` from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != src_hash:
+    if rec.get("kernel_source_hash") != src_hash:
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    k = rec.get("ops", {}).get(op)
+    return None if k is None else k.get("hbm_bytes_per_call")
+
+
+def _pmc_rows(csv_path: str, counter: str):
+    """(dispatch id, kernel name, value) of one counter from a rocprofv3 --pmc CSV."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            name = r["Kernel_Name"]
+            out[key] = (name, out.get(key, (name, 0.0))[1] + float(r["Counter_Value"]))
+    return [(k, v[0], v[1]) for k, v in sorted(out.items())]
+
+
+def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, command: str) -> dict:
+    """HBM bytes per C-ABI call from two rocprofv3 --pmc runs of this benchmark
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain device copy of COPY_CAL_BYTES that
+    --copy-calibration enqueues after the timed steps."""
+    rec = {"kernel_source_hash": kernel_source_hash(), "command": command,
+           "copy_calibration_bytes": COPY_CAL_BYTES, "ops": {}}
+    calls = steps + warmup
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, counter)
+        # the calibration copy is the first runtime copy-kernel dispatch after the
+        # last library kernel: --copy-calibration enqueues it right after the steps
+        last_lib = max(d for d, n, _ in rows if "moonep" in n)
+        copies = [v for d, n, v in rows if d > last_lib and "copyBuffer" in n]
+        if not copies:
+            raise SystemExit(f"{path}: no copy-kernel dispatch for the calibration")
+        cal_kib = copies[0]
+        factor = COPY_CAL_BYTES / (cal_kib * 1024.0)
+        rec[counter.lower() + "_copy_kib"] = cal_kib
+        rec[counter.lower() + "_scale"] = factor
+        for op, kernels in OP_KERNELS.items():
+            tot = sum(v for _, n, v in rows if any(k + "(" in n or k + "<" in n for k in kernels))
+            ent = rec["ops"].setdefault(op, {})
+            ent[counter.lower() + "_bytes_per_call"] = tot * 1024.0 * factor / calls
+    for ent in rec["ops"].values():
+        ent["hbm_bytes_per_call"] = ent["fetch_size_bytes_per_call"] + ent["write_size_bytes_per_call"]
+    return rec
 
 
 def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
@@ -127,7 +177,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"after the timed steps, one plain device copy of {COPY_CAL_BYTES} bytes "
+                         "(the reference dispatch for scaling HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs "
+                         "of a run with --copy-calibration (same --steps/--warmup), then exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiled command, recorded in the traffic summary")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        rec = traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.steps,
+                               args.warmup, args.traffic_command)
+        with open(TRAFFIC_PATH, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(rec, indent=1, sort_keys=True))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
@@ -197,6 +264,13 @@ def main():
     op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, op in enumerate(ops)}
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        a = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        print(f"# copy calibration: {COPY_CAL_BYTES} bytes", file=sys.stderr, flush=True)
 
     v = td.plan_views(dims, plan_buf)
     n_dup = v["n_dup"].cpu().numpy()
@@ -220,9 +294,12 @@ def main():
     src_hash = kernel_source_hash()
     traffic = traffic_for(dom, src_hash)
     roofline = {"bound": "hbm", "achieved": round(gbs[dom], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs[dom] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "unit": "GB/s", "frac": round(gbs[dom] / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": dom, "algorithmic_bytes_per_launch": nbytes[dom],
-                "avg_launch_ms": round(op_ms[dom], 4)}
+                "avg_launch_ms": round(op_ms[dom], 4),
+                "launch": f"one moonep_{dom} call: a short sequence of k_{dom} launches "
+                          "over token chunks, timed as a whole"}
 
     cpu = None
     if not args.no_cpu_baseline:
