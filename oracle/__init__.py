@@ -15,6 +15,10 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   combine   -- pinned: closed forms, binary64 error bound, library bf16 rounding
   reduce    -- pinned: hand-derived rounding-order value, integer closed form,
                binary64 error bound
+  combine_backward_y, combine_backward_w, dispatch_backward
+            -- pinned: torch autograd in binary64 of the plain forward
+               definitions (gather, weighted sum), torch's bf16 rounding, closed
+               forms (unit weights, K copies of a bf16 row), binary64 error bounds
 """
 from __future__ import annotations
 
@@ -77,6 +81,12 @@ def _load() -> ctypes.CDLL:
         lib.oracle_reduce.restype = None
         lib.oracle_f32_to_bf16.argtypes = [i64, vp, vp]
         lib.oracle_f32_to_bf16.restype = None
+        lib.oracle_combine_backward_y.argtypes = [i64, i32, i64, i32, i32, vp, vp, vp, i64, i64, vp]
+        lib.oracle_combine_backward_y.restype = None
+        lib.oracle_combine_backward_w.argtypes = [i64, i32, i64, i32, i32, vp, vp, vp, vp]
+        lib.oracle_combine_backward_w.restype = None
+        lib.oracle_dispatch_backward.argtypes = [i64, i32, i64, i32, i32, vp, vp, vp]
+        lib.oracle_dispatch_backward.restype = None
         _lib = lib
     return _lib
 
@@ -194,3 +204,57 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     y = np.zeros(x.size, dtype=np.uint16)
     lib.oracle_f32_to_bf16(x.size, _ptr(x), _ptr(y))
     return y
+
+
+def _row_type(dtype: int):
+    return np.uint16 if dtype == BF16 else np.float32
+
+
+def combine_backward_y(dst: np.ndarray, K: int, grad_out: np.ndarray, w: np.ndarray,
+                       gout_dtype: int, y_dtype: int, slot_lo: int = 0,
+                       slot_hi: Optional[int] = None, fill=0) -> np.ndarray:
+    """grad_y rows for slots [slot_lo, slot_hi) (all slots by default): grad_out is
+    [n_tok, H] float32 or bf16 bits; slots holding no entry keep `fill`."""
+    lib = _load()
+    grad_out = np.ascontiguousarray(grad_out)
+    assert grad_out.dtype == _row_type(gout_dtype)
+    dst = np.ascontiguousarray(dst, dtype=np.int32).reshape(-1)
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    H = grad_out.shape[-1]
+    if slot_hi is None:
+        slot_hi = dst.size
+    out = np.full((slot_hi - slot_lo, H), fill, dtype=_row_type(y_dtype))
+    lib.oracle_combine_backward_y(dst.size, K, H, gout_dtype, y_dtype, _ptr(grad_out), _ptr(w),
+                                  _ptr(dst), slot_lo, slot_hi, _ptr(out))
+    return out
+
+
+def combine_backward_w(dst: np.ndarray, K: int, grad_out: np.ndarray, y_rows: np.ndarray,
+                       gout_dtype: int, y_dtype: int) -> np.ndarray:
+    """grad_w [n_tok*K] in binary64; y_rows[a] is the expert-output row of entry a."""
+    lib = _load()
+    grad_out = np.ascontiguousarray(grad_out)
+    y_rows = np.ascontiguousarray(y_rows)
+    assert grad_out.dtype == _row_type(gout_dtype) and y_rows.dtype == _row_type(y_dtype)
+    dst = np.ascontiguousarray(dst, dtype=np.int32).reshape(-1)
+    n_tok, H = grad_out.shape
+    assert dst.size == n_tok * K and y_rows.shape == (dst.size, H)
+    gw = np.zeros(dst.size, dtype=np.float64)
+    lib.oracle_combine_backward_w(n_tok, K, H, gout_dtype, y_dtype, _ptr(grad_out), _ptr(y_rows),
+                                  _ptr(dst), _ptr(gw))
+    return gw
+
+
+def dispatch_backward(dst: np.ndarray, K: int, grad_recv: np.ndarray, in_dtype: int,
+                      out_dtype: int) -> np.ndarray:
+    """grad_hidden [n_tok, H]: grad_recv is [n_slots, H] float32 or bf16 bits."""
+    lib = _load()
+    grad_recv = np.ascontiguousarray(grad_recv)
+    assert grad_recv.dtype == _row_type(in_dtype)
+    dst = np.ascontiguousarray(dst, dtype=np.int32).reshape(-1)
+    H = grad_recv.shape[-1]
+    n_tok = dst.size // K
+    out = np.zeros((n_tok, H), dtype=_row_type(out_dtype))
+    lib.oracle_dispatch_backward(n_tok, K, H, in_dtype, out_dtype, _ptr(grad_recv), _ptr(dst),
+                                 _ptr(out))
+    return out

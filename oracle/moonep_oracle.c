@@ -305,3 +305,83 @@ void oracle_f32_to_bf16(int64_t n, const float *x, uint16_t *y)
 {
     for (int64_t i = 0; i < n; ++i) y[i] = f32_to_bf16_rne(x[i]);
 }
+
+/* ---------------------------------------------------------------- backward
+ * The forward moves are linear maps, and training (the pages speak of gradients
+ * reduced back to home on the backward pass, news.hamidun.com EN, "How MoonEP
+ * works") needs their adjoints:
+ *   combine  out[g] = sum_k w[g,k] * y[dst(g,k)]
+ *     grad_y[dst(g,k)] = w[g,k] * grad_out[g]          (one binary32 multiply,
+ *                                                      stored in y's type)
+ *     grad_w[g,k]      = sum_i grad_out[g][i] * y[dst(g,k)][i]   (binary64 here)
+ *   dispatch recv[dst(a)] = hidden[a / K]
+ *     grad_hidden[g]   = sum_k grad_recv[dst(g,k)]      (binary32 adds in
+ *                                                      ascending k from +0.0)
+ * Entries with dst < 0 contribute nothing; their grad_w is 0.
+ */
+static float load_elem(const void *base, int32_t dtype, int64_t idx)
+{
+    return dtype == DT_BF16 ? bf16_to_f32(((const uint16_t *)base)[idx]) : ((const float *)base)[idx];
+}
+
+static void store_elem(void *base, int32_t dtype, int64_t idx, float v)
+{
+    if (dtype == DT_BF16) ((uint16_t *)base)[idx] = f32_to_bf16_rne(v);
+    else ((float *)base)[idx] = v;
+}
+
+/* grad_y rows for slots [slot_lo, slot_hi) into grad_y_window (row 0 = slot_lo).
+   Slots that hold no entry are not written. */
+void oracle_combine_backward_y(int64_t n_ent, int32_t K, int64_t H, int32_t gout_dtype,
+                               int32_t y_dtype, const void *grad_out, const float *w,
+                               const int32_t *dst, int64_t slot_lo, int64_t slot_hi,
+                               void *grad_y_window)
+{
+    for (int64_t a = 0; a < n_ent; ++a) {
+        int64_t d = dst[a];
+        if (d < slot_lo || d >= slot_hi) continue;
+        int64_t g = a / K;
+        for (int64_t i = 0; i < H; ++i) {
+            float x = load_elem(grad_out, gout_dtype, g * H + i);
+            float v = w[a] * x;
+            store_elem(grad_y_window, y_dtype, (d - slot_lo) * H + i, v);
+        }
+    }
+}
+
+/* grad_w[a] for tokens g in [0, n_tok), a = g*K + k, in binary64. y_rows holds the
+   expert-output row of every entry: y_rows[a] = y[dst(a)] (a caller may gather
+   just the rows it samples); entries with dst < 0 give 0. */
+void oracle_combine_backward_w(int64_t n_tok, int32_t K, int64_t H, int32_t gout_dtype,
+                               int32_t y_dtype, const void *grad_out, const void *y_rows,
+                               const int32_t *dst, double *grad_w)
+{
+    for (int64_t g = 0; g < n_tok; ++g)
+        for (int k = 0; k < K; ++k) {
+            int64_t a = g * K + k;
+            double s = 0.0;
+            if (dst[a] >= 0)
+                for (int64_t i = 0; i < H; ++i)
+                    s += (double)load_elem(grad_out, gout_dtype, g * H + i) *
+                         (double)load_elem(y_rows, y_dtype, a * H + i);
+            grad_w[a] = s;
+        }
+}
+
+/* grad_hidden[g] = sum over k of grad_recv[dst(g,k)], binary32 adds in ascending k
+   from +0.0, stored as out_dtype. */
+void oracle_dispatch_backward(int64_t n_tok, int32_t K, int64_t H, int32_t in_dtype,
+                              int32_t out_dtype, const void *grad_recv, const int32_t *dst,
+                              void *grad_hidden)
+{
+    for (int64_t g = 0; g < n_tok; ++g)
+        for (int64_t i = 0; i < H; ++i) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int64_t d = dst[g * K + k];
+                if (d < 0) continue;
+                acc = acc + load_elem(grad_recv, in_dtype, d * H + i);
+            }
+            store_elem(grad_hidden, out_dtype, g * H + i, acc);
+        }
+}
