@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine GB/s (% of HBM peak) + plan latency µs, K3 shape, 1 GPU"
 KERNEL_SOURCES = ("token_dispatch_amd/csrc/move.hip", "token_dispatch_amd/csrc/plan.hip",
-                  "token_dispatch_amd/csrc/api.hip", "token_dispatch_amd/csrc/internal.h")
+                  "token_dispatch_amd/csrc/api.hip", "token_dispatch_amd/csrc/internal.h",
+                  "token_dispatch_amd/csrc/backward.hip", "token_dispatch_amd/csrc/rows.h")
 
 
 def kernel_source_hash() -> str:
@@ -45,7 +46,11 @@ def algorithmic_bytes(wl, n_mat, n_xm):
     rep = 2 * n_mat * wl.block_bytes
     red = (n_mat + 2 * n_xm) * wl.block_elems * 4
     plan = 12 * wl.n_ent
-    return {"dispatch": d, "combine": c, "replicate": rep, "reduce": red, "plan": plan}
+    # backward: grad_out read once, y read, grad_y written, w / grad_w / dst
+    cb = 2 * wl.n_ent * row + wl.n_tok * row + 12 * wl.n_ent
+    db = wl.n_ent * row + wl.n_tok * row + 4 * wl.n_ent
+    return {"dispatch": d, "combine": c, "replicate": rep, "reduce": red, "plan": plan,
+            "combine_backward": cb, "dispatch_backward": db}
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
@@ -53,6 +58,8 @@ TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
 # Library kernels behind each C-ABI call (one call may enqueue several launches).
 OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_assign"), "replicate": ("k_replicate",),
               "dispatch": ("k_dispatch",), "combine": ("k_combine",), "reduce": ("k_reduce",)}
+# (k_combine also serves the backward of dispatch, so traffic is only summed for
+# runs without --with-backward)
 COPY_CAL_BYTES = 1 << 30
 
 
@@ -177,6 +184,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="also time combine-backward (grad_out = out, y = recv) and "
+                         "dispatch-backward (grad_recv = grad_y) in every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after the timed steps, one plain device copy of {COPY_CAL_BYTES} bytes "
                          "(the reference dispatch for scaling HBM byte counters)")
@@ -223,11 +233,17 @@ def main():
     dup_w = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=expert_w.dtype, device=dev)
     dup_g, home_g = W.make_grads(wl, args.seed, dev)
     plan_buf = td.new_plan_buffer(dims, dev)
+    if args.with_backward:
+        grad_y = torch.empty_like(recv)
+        grad_w = torch.empty((wl.R, wl.S, wl.K), dtype=torch.float32, device=dev)
+        grad_h = torch.empty_like(hidden)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     print("# inputs resident", file=sys.stderr, flush=True)
 
     ops = ["plan", "replicate", "dispatch", "combine", "reduce"]
+    if args.with_backward:
+        ops += ["combine_backward", "dispatch_backward"]
 
     def step(ev=None):
         if ev:
@@ -247,13 +263,21 @@ def main():
         td.moonep_reduce_dup_grads(dims, plan_buf, dup_g, home_g, wl.block_elems)
         if ev:
             ev[5].record(stream)
+        if args.with_backward:
+            td.moonep_combine_backward(dims, plan_buf, out, w_d, recv, grad_y, grad_w)
+            if ev:
+                ev[6].record(stream)
+            td.moonep_dispatch_backward(dims, plan_buf, grad_y, grad_h)
+            if ev:
+                ev[7].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"# warmup {args.warmup} done", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

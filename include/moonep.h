@@ -206,6 +206,47 @@ int moonep_reduce_dup_grads(const moonep_dims *dims, const void *plan_buf,
                             const float *dup_grads, float *home_grads, int64_t block_elems,
                             void *stream);
 
+/*
+ * moonep_combine_backward -- gradients of combine for the backward pass. The
+ * layer is trained, and its duplicate experts receive gradients on the backward
+ * pass (news.hamidun.com EN, "How MoonEP works"); these are the adjoints of the
+ * weighted sum that moonep_combine computes.
+ *
+ *   grad_out    [R, S, H] of gout_dtype, read: gradient of combine's output
+ *   gout_dtype  MOONEP_F32 or MOONEP_BF16 (H * its size a multiple of 16 bytes)
+ *   topk_w      float32 [R, S, K], read (may be NULL when grad_y is NULL)
+ *   y           [R, S*K, H] of dims->dtype, read: the forward expert outputs
+ *               (may be NULL when grad_w is NULL)
+ *   grad_y      [R, S*K, H] of dims->dtype, written, or NULL to skip:
+ *               grad_y[dst[a]] = topk_w[a] * grad_out[a / K], one binary32
+ *               multiply per element, stored as dims->dtype (bf16: nearest even);
+ *               slots that hold no entry are left untouched
+ *   grad_w      float32 [R, S, K], written, or NULL to skip:
+ *               grad_w[a] = sum over i of grad_out[a / K][i] * y[dst[a]][i],
+ *               accumulated in binary32 in a fixed order (so within
+ *               H * 2^-24 * sum |grad_out * y| of the exact value); 0 for a
+ *               dropped entry
+ * With both outputs NULL the call only checks its dims and returns MOONEP_OK.
+ */
+int moonep_combine_backward(const moonep_dims *dims, const void *plan_buf, const void *grad_out,
+                            int32_t gout_dtype, const float *topk_w, const void *y, void *grad_y,
+                            float *grad_w, void *stream);
+
+/*
+ * moonep_dispatch_backward -- gradient of dispatch: each token row was copied
+ * to its K slots ("Why this matters to engineers", news.hamidun.com EN), so its
+ * gradient is the sum of the K slot gradients.
+ *
+ *   grad_recv    [R, S*K, H] of dims->dtype, read
+ *   grad_hidden  [R, S, H] of out_dtype, written:
+ *                grad_hidden[g] = sum over k = 0..K-1 of grad_recv[dst[g*K+k]],
+ *                binary32 adds in ascending k from +0.0, then stored (bf16:
+ *                nearest even); dropped entries contribute nothing
+ *   out_dtype    MOONEP_F32 or MOONEP_BF16
+ */
+int moonep_dispatch_backward(const moonep_dims *dims, const void *plan_buf, const void *grad_recv,
+                             void *grad_hidden, int32_t out_dtype, void *stream);
+
 /* Text of a return value. Never NULL; the string is static. */
 const char *moonep_strerror(int rc);
 

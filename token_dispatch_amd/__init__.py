@@ -30,7 +30,8 @@ BF16 = 1
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 
 ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_dispatch", "moonep_replicate",
-                "moonep_combine", "moonep_reduce_dup_grads", "moonep_strerror")
+                "moonep_combine", "moonep_reduce_dup_grads", "moonep_combine_backward",
+                "moonep_dispatch_backward", "moonep_strerror")
 
 
 class Dims(ctypes.Structure):
@@ -66,6 +67,8 @@ _lib.moonep_dispatch.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp]
 _lib.moonep_replicate.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
 _lib.moonep_combine.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp, _i32, _vp]
 _lib.moonep_reduce_dup_grads.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
+_lib.moonep_combine_backward.argtypes = [_P_DIMS, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.moonep_dispatch_backward.argtypes = [_P_DIMS, _vp, _vp, _vp, _i32, _vp]
 _lib.moonep_strerror.argtypes = [ctypes.c_int]
 _lib.moonep_strerror.restype = ctypes.c_char_p
 for _n in ENTRY_POINTS[:-1]:
@@ -177,6 +180,41 @@ def moonep_reduce_dup_grads(dims: Dims, plan_buf, dup_grads, home_grads, block_e
         _ptr(dup_grads, "dup_grads", torch.float32, 4 * dims.R * dims.B * block_elems),
         _ptr(home_grads, "home_grads", torch.float32, 4 * dims.E * block_elems),
         int(block_elems), _stream(stream, home_grads)), "moonep_reduce_dup_grads")
+
+
+def moonep_combine_backward(dims: Dims, plan_buf, grad_out, topk_w, y, grad_y, grad_w,
+                            stream=None) -> None:
+    """grad_out's dtype (float32 or bfloat16) is passed as gout_dtype; grad_y or
+    grad_w may be None to skip that output (then topk_w or y may be None)."""
+    torch = _torch()
+    g_dt = BF16 if grad_out.dtype == torch.bfloat16 else F32
+    grow = dims.H * (2 if g_dt == BF16 else 4)
+    row = dims.H * (2 if dims.dtype == BF16 else 4)
+    n_ent = dims.R * dims.S * dims.K
+    lay = moonep_plan_layout(dims)
+    ref = grad_y if grad_y is not None else grad_out
+    _check(_lib.moonep_combine_backward(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(grad_out, "grad_out", None, dims.R * dims.S * grow), g_dt,
+        None if grad_y is None else _ptr(topk_w, "topk_w", torch.float32, 4 * n_ent),
+        None if grad_w is None else _ptr(y, "y", _row_dtype(dims), n_ent * row),
+        None if grad_y is None else _ptr(grad_y, "grad_y", _row_dtype(dims), n_ent * row),
+        None if grad_w is None else _ptr(grad_w, "grad_w", torch.float32, 4 * n_ent),
+        _stream(stream, ref)), "moonep_combine_backward")
+
+
+def moonep_dispatch_backward(dims: Dims, plan_buf, grad_recv, grad_hidden,
+                             out_dtype: Optional[int] = None, stream=None) -> None:
+    torch = _torch()
+    od = dims.dtype if out_dtype is None else int(out_dtype)
+    row = dims.H * (2 if dims.dtype == BF16 else 4)
+    orow = dims.H * (2 if od == BF16 else 4)
+    lay = moonep_plan_layout(dims)
+    _check(_lib.moonep_dispatch_backward(
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        _ptr(grad_recv, "grad_recv", _row_dtype(dims), dims.R * dims.S * dims.K * row),
+        _ptr(grad_hidden, "grad_hidden", torch.bfloat16 if od == BF16 else torch.float32,
+             dims.R * dims.S * orow), od, _stream(stream, grad_hidden)), "moonep_dispatch_backward")
 
 
 # ------------------------------------------------------------- buffer helpers

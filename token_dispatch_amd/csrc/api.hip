@@ -217,6 +217,43 @@ int moonep_reduce_dup_grads(const moonep_dims *d, const void *plan_buf, const fl
                                    home_grads, block_elems, static_cast<hipStream_t>(stream)));
 }
 
+int moonep_combine_backward(const moonep_dims *d, const void *plan_buf, const void *grad_out,
+                            int32_t gout_dtype, const float *topk_w, const void *y, void *grad_y,
+                            float *grad_w, void *stream) {
+    moonep_layout l;
+    int rc = moonep_plan_layout(d, &l);
+    if (rc != MOONEP_OK) return rc;
+    if (gout_dtype != MOONEP_F32 && gout_dtype != MOONEP_BF16) return MOONEP_ERR_DIMS;
+    // grad_out rows must also split into 16-byte chunks
+    if ((d->H * elem_bytes(gout_dtype)) % 16 != 0) return MOONEP_ERR_DIMS;
+    if (grad_y == nullptr && grad_w == nullptr) return MOONEP_OK;  // nothing asked for
+    if (!aligned16(plan_buf) || !aligned16(grad_out)) return MOONEP_ERR_PTR;
+    if (grad_y != nullptr && (!aligned16(grad_y) || !aligned16(topk_w))) return MOONEP_ERR_PTR;
+    if (grad_w != nullptr && (!aligned16(grad_w) || !aligned16(y))) return MOONEP_ERR_PTR;
+    const PlanShape sh = shape_of(d, l);
+    (void)hipGetLastError();
+    return launch_rc(launch_combine_backward(sh, resolve(l, const_cast<void *>(plan_buf)), grad_out,
+                                             gout_dtype == MOONEP_BF16, topk_w, y, grad_y, grad_w,
+                                             d->dtype == MOONEP_BF16, d->H,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int moonep_dispatch_backward(const moonep_dims *d, const void *plan_buf, const void *grad_recv,
+                             void *grad_hidden, int32_t out_dtype, void *stream) {
+    moonep_layout l;
+    int rc = moonep_plan_layout(d, &l);
+    if (rc != MOONEP_OK) return rc;
+    if (out_dtype != MOONEP_F32 && out_dtype != MOONEP_BF16) return MOONEP_ERR_DIMS;
+    if (!aligned16(plan_buf) || !aligned16(grad_recv) || !aligned16(grad_hidden))
+        return MOONEP_ERR_PTR;
+    const PlanShape sh = shape_of(d, l);
+    (void)hipGetLastError();
+    return launch_rc(launch_dispatch_backward(sh, resolve(l, const_cast<void *>(plan_buf)),
+                                              grad_recv, grad_hidden, d->dtype == MOONEP_BF16,
+                                              out_dtype == MOONEP_BF16, d->H,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char *moonep_strerror(int rc) {
     switch (rc) {
         case MOONEP_OK: return "ok";

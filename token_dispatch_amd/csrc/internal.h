@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (api.hip) and the kernel
-// translation units (plan.hip, move.hip). Not installed, not part of the ABI.
+// translation units (plan.hip, move.hip, backward.hip). Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,6 +49,17 @@ hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *h
 hipError_t launch_combine(const PlanShape &sh, const PlanPtrs &p, const void *y,
                           const float *w, void *out, int in_bf16, int out_bf16, int64_t H,
                           hipStream_t st);
+
+// The backward of dispatch: combine with unit weights (move.hip).
+hipError_t launch_dispatch_backward(const PlanShape &sh, const PlanPtrs &p, const void *grad_recv,
+                                    void *grad_hidden, int in_bf16, int out_bf16, int64_t H,
+                                    hipStream_t st);
+
+// The backward of combine (backward.hip): grad_w first (skipped when NULL), then
+// grad_y (skipped when NULL).
+hipError_t launch_combine_backward(const PlanShape &sh, const PlanPtrs &p, const void *grad_out,
+                                   int gout_bf16, const float *w, const void *y, void *grad_y,
+                                   float *grad_w, int y_bf16, int64_t H, hipStream_t st);
 
 hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *expert_w,
                             void *dup_w, int64_t block_bytes, hipStream_t st);

@@ -27,31 +27,12 @@
 //           walks (expert with duplicates, block piece); each element is summed
 //           home first, then duplicates in ascending rank.
 #include "internal.h"
+#include "rows.h"
 
 namespace moonep {
 namespace {
 
-// Native 16-byte vector: what global_load/store_dwordx4 move, and what the
-// non-temporal store builtin accepts.
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-constexpr int kMoveThreads = 256;
-constexpr int kMoveWaves = kMoveThreads / 64;
-
-__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
-
-__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ __forceinline__ float readlane_f(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Round binary32 to bf16, nearest-even; NaN becomes a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+using namespace rows;
 
 // ---------------------------------------------------------------- dispatch
 // Work item = (token, segment of 64*CPL chunks). C = 16-byte chunks per row.
@@ -103,58 +84,10 @@ __global__ __launch_bounds__(kMoveThreads) void k_dispatch(const v4u *__restrict
 }
 
 // ---------------------------------------------------------------- combine
-template <bool IN_BF16>
-struct Chunk;
-template <>
-struct Chunk<true> {  // 8 bf16
-    static constexpr int N = 8;
-    __device__ static void unpack(const v4u &q, float *x) {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[2 * j] = __uint_as_float(w[j] << 16);
-            x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-        }
-    }
-};
-template <>
-struct Chunk<false> {  // 4 f32
-    static constexpr int N = 4;
-    __device__ static void unpack(const v4u &q, float *x) {
-        x[0] = __uint_as_float(q.x);
-        x[1] = __uint_as_float(q.y);
-        x[2] = __uint_as_float(q.z);
-        x[3] = __uint_as_float(q.w);
-    }
-};
-
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-// Store N accumulators (elements elem0 .. elem0+N-1 of out) non-temporally.
-template <int N, bool OUT_BF16>
-__device__ __forceinline__ void store_elems(void *out, int64_t elem0, const float *a) {
-    if constexpr (OUT_BF16) {
-        uint32_t w[N / 2];
-#pragma unroll
-        for (int j = 0; j < N / 2; ++j) w[j] = bf16_rne(a[2 * j]) | (bf16_rne(a[2 * j + 1]) << 16);
-        uint16_t *o = reinterpret_cast<uint16_t *>(out) + elem0;
-        if constexpr (N == 8) {
-            __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u *>(o));
-        } else {
-            __builtin_nontemporal_store(v2u{w[0], w[1]}, reinterpret_cast<v2u *>(o));
-        }
-    } else {
-        float *o = reinterpret_cast<float *>(out) + elem0;
-#pragma unroll
-        for (int j = 0; j < N; j += 4)
-            __builtin_nontemporal_store(v4f{a[j], a[j + 1], a[j + 2], a[j + 3]},
-                                        reinterpret_cast<v4f *>(o + j));
-    }
-}
-
 // One wave per work item (token, row segment) of the launch's range [i_lo, i_hi).
-template <int CPL, bool IN_BF16, bool OUT_BF16>
+// UNIT_W: every weight is 1 and w is not read; fma(1, x, acc) is the binary32
+// sum acc + x, which makes this the backward of dispatch.
+template <int CPL, bool IN_BF16, bool OUT_BF16, bool UNIT_W>
 __global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict__ y,
                                                           const float *__restrict__ w,
                                                           const int32_t *__restrict__ dst,
@@ -171,7 +104,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict_
     const int seg = (int)(item - tok * segs);
     const int cbase = seg * 64 * CPL + lane;
     const int my_dst = lane < K ? dst[tok * K + lane] : -1;
-    const float my_w = lane < K ? w[tok * K + lane] : 0.0f;
+    const float my_w = UNIT_W ? 1.0f : (lane < K ? w[tok * K + lane] : 0.0f);
 
     float acc[CPL][N];
 #pragma unroll
@@ -201,7 +134,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict_
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = cbase + i * 64;
-        if (c < C) store_elems<N, OUT_BF16>(out, (tok * C + c) * N, acc[i]);
+        if (c < C) store_elems<N, OUT_BF16, true>(out, (tok * C + c) * N, acc[i]);
     }
 }
 
@@ -294,53 +227,17 @@ __global__ __launch_bounds__(kMoveThreads) void k_reduce(
     }
 }
 
-// Chunks per lane of one row segment: the row is split into the fewest segments
-// of at most 16 chunks per lane, then each segment takes an instantiated width.
-int pick_cpl(int64_t C) {
-    const int64_t per_lane = (C + 63) / 64;
-    const int64_t segs = (per_lane + 15) / 16;
-    const int64_t need = (per_lane + segs - 1) / segs;
-    static const int widths[] = {1, 2, 4, 7, 8, 14, 16};
-    for (int w : widths)
-        if (w >= need) return w;
-    return 16;
-}
-
 // Grid of the fixed-size copy kernels: enough workgroups to fill 256 CUs.
 constexpr int kCopyGrid = 256 * 8;
 
 }  // namespace
 
-// Row segments of a dispatch wave, by chunks per lane: as many as fit in about
-// 200 VGPRs of row data, which keeps two waves per SIMD resident.
-constexpr int tpw_of(int cpl) { return cpl >= 14 ? 3 : cpl >= 8 ? 6 : cpl >= 7 ? 7 : 8; }
-
-// Workgroups of k_dispatch<CPL, TPW> that the current device holds at once.
-template <int CPL>
-int resident_dispatch_wgs() {
-    static int cached[64];  // per device; 0 = not yet queried (benign race: same value)
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
-    if (v > 0) return v;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_dispatch<CPL, tpw_of(CPL)>,
-                                                     kMoveThreads, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    v = cus * per_cu;
-    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
-    return v;
-}
-
 template <int CPL>
 hipError_t dispatch_chunks(const v4u *h, v4u *r, const int32_t *dst, int64_t items, int32_t segs,
                            int32_t C, int32_t K, int64_t n_slots, hipStream_t st) {
     constexpr int TPW = tpw_of(CPL);
-    const int64_t full = resident_dispatch_wgs<CPL>();
+    static int cache[64];
+    const int64_t full = resident_wgs(k_dispatch<CPL, TPW>, cache);
     const int64_t per_launch = full * kMoveWaves * TPW;
     for (int64_t lo = 0; lo < items; lo += per_launch) {
         const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
@@ -380,7 +277,7 @@ hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *h
 // stay small, small enough that the chunk's stores come as one burst.
 constexpr int64_t kCombineChunkOutBytes = 56ll << 20;
 
-template <int CPL, bool IB, bool OB>
+template <int CPL, bool IB, bool OB, bool UW>
 hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void *out,
                           int64_t n_tok, int32_t segs, int32_t C, int32_t K, int64_t n_slots,
                           int64_t out_row_bytes, hipStream_t st) {
@@ -391,7 +288,7 @@ hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void
     for (int64_t lo = 0; lo < items; lo += per_launch) {
         const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
         const dim3 grid((unsigned)((hi - lo + kMoveWaves - 1) / kMoveWaves));
-        hipLaunchKernelGGL((k_combine<CPL, IB, OB>), grid, dim3(kMoveThreads), 0, st, y, w, dst,
+        hipLaunchKernelGGL((k_combine<CPL, IB, OB, UW>), grid, dim3(kMoveThreads), 0, st, y, w, dst,
                            out, lo, hi, segs, C, K, n_slots);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -399,7 +296,7 @@ hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void
     return hipSuccess;
 }
 
-template <bool IB, bool OB>
+template <bool IB, bool OB, bool UW>
 static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const void *y,
                                 const float *w, void *out, int64_t C, int64_t H, hipStream_t st) {
     const int cpl = pick_cpl(C);
@@ -409,7 +306,7 @@ static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const vo
     auto yy = static_cast<const v4u *>(y);
 #define MOONEP_COMBINE(W)                                                                  \
     case W:                                                                                \
-        return combine_chunks<W, IB, OB>(yy, w, p.dst, out, sh.n_tok, segs, (int32_t)C, sh.K, \
+        return combine_chunks<W, IB, OB, UW>(yy, w, p.dst, out, sh.n_tok, segs, (int32_t)C, sh.K, \
                                          n_slots, orow, st);
     switch (cpl) {
         MOONEP_COMBINE(1)
@@ -428,10 +325,22 @@ hipError_t launch_combine(const PlanShape &sh, const PlanPtrs &p, const void *y,
                           const float *w, void *out, int in_bf16, int out_bf16, int64_t H,
                           hipStream_t st) {
     const int64_t C = H * (in_bf16 ? 2 : 4) / 16;
-    if (in_bf16 && out_bf16) return combine_typed<true, true>(sh, p, y, w, out, C, H, st);
-    if (in_bf16) return combine_typed<true, false>(sh, p, y, w, out, C, H, st);
-    if (out_bf16) return combine_typed<false, true>(sh, p, y, w, out, C, H, st);
-    return combine_typed<false, false>(sh, p, y, w, out, C, H, st);
+    if (in_bf16 && out_bf16) return combine_typed<true, true, false>(sh, p, y, w, out, C, H, st);
+    if (in_bf16) return combine_typed<true, false, false>(sh, p, y, w, out, C, H, st);
+    if (out_bf16) return combine_typed<false, true, false>(sh, p, y, w, out, C, H, st);
+    return combine_typed<false, false, false>(sh, p, y, w, out, C, H, st);
+}
+
+hipError_t launch_dispatch_backward(const PlanShape &sh, const PlanPtrs &p, const void *grad_recv,
+                                    void *grad_hidden, int in_bf16, int out_bf16, int64_t H,
+                                    hipStream_t st) {
+    const int64_t C = H * (in_bf16 ? 2 : 4) / 16;
+    const void *g = grad_recv;
+    void *o = grad_hidden;
+    if (in_bf16 && out_bf16) return combine_typed<true, true, true>(sh, p, g, nullptr, o, C, H, st);
+    if (in_bf16) return combine_typed<true, false, true>(sh, p, g, nullptr, o, C, H, st);
+    if (out_bf16) return combine_typed<false, true, true>(sh, p, g, nullptr, o, C, H, st);
+    return combine_typed<false, false, true>(sh, p, g, nullptr, o, C, H, st);
 }
 
 hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *expert_w,
