@@ -118,7 +118,7 @@ typedef struct moonep_layout {
     int64_t status, maxT, maxvio, T, hoff, L, keep, O, D, Opre, Dpre, dst, src;
     int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
     int64_t n_list, list_expert, list_rank, list_b, dup_ptr;
-    int64_t ws_tile_counts, ws_tile_status, ws_mat_pre, ws_xlist, ws_n_x;
+    int64_t ws_tile_counts, ws_tile_status, ws_mat_pre, ws_xlist, ws_n_x, ws_piece_js;
 } moonep_layout;
 
 /* Fills *out for dims. Pure host computation. Returns MOONEP_OK or

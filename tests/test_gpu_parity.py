@@ -56,6 +56,8 @@ SMALL = [
     # rows longer than one 16-chunk-per-lane segment (two segments)
     _wl("long_row", 2, 16, 2, 200, 2, 12288, W.BF16, 2.0),
     _wl("e1024", 8, 1024, 8, 600, 128, 64, W.BF16, 2.0),
+    # the largest rank and expert counts: one home expert per rank, 1024 ranks
+    _wl("r1024", 1024, 1024, 2, 4, 2, 8, W.BF16, 2.0),
     # fp32 rows and a larger fp32 weight block
     _wl("f32_wide", 4, 16, 2, 1000, 4, 1024, W.F32, 2.5, block=(3, 64, 64)),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks

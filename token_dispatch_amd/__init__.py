@@ -50,7 +50,7 @@ _LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D
                    "Dpre", "dst", "src", "n_dup", "dup_expert", "dup_start", "dup_count",
                    "seg_ptr", "seg_expert", "n_list", "list_expert", "list_rank", "list_b",
                    "dup_ptr", "ws_tile_counts", "ws_tile_status", "ws_mat_pre", "ws_xlist",
-                   "ws_n_x")
+                   "ws_n_x", "ws_piece_js")
 
 
 class Layout(ctypes.Structure):

@@ -86,6 +86,7 @@ PlanPtrs resolve(const moonep_layout &l, void *base) {
     p.mat_pre = at(l.ws_mat_pre);
     p.xlist = at(l.ws_xlist);
     p.n_x = at(l.ws_n_x);
+    p.piece_js = at(l.ws_piece_js);
     return p;
 }
 
@@ -144,6 +145,7 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     l.ws_mat_pre = take(4 * (R + 1));
     l.ws_xlist = take(4 * E);
     l.ws_n_x = take(4);
+    l.ws_piece_js = take(4 * (int64_t)l.pcap);
     l.bytes = off;
     *out = l;
     return MOONEP_OK;

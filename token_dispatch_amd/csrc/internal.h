@@ -24,7 +24,7 @@ struct PlanPtrs {
     int32_t *T, *hoff, *L, *keep, *O, *D, *Opre, *Dpre, *dst, *src;
     int32_t *n_dup, *dup_expert, *dup_start, *dup_count, *seg_ptr, *seg_expert;
     int32_t *n_list, *list_expert, *list_rank, *list_b, *dup_ptr;
-    int32_t *tile_counts, *tile_status, *mat_pre, *xlist, *n_x;
+    int32_t *tile_counts, *tile_status, *mat_pre, *xlist, *n_x, *piece_js;
 };
 
 // Shape constants every kernel needs, computed once on the host.

@@ -7,39 +7,52 @@
 // blog.schoergendorfer.com, "The problem MoonEP targets").
 //
 // Four launches, every grid fixed by the dims alone (no host round trip):
-//   k_count   one workgroup per token tile: validates ids, builds the tile's
-//             expert histogram in LDS, writes it to tile_counts[tile][E].
+//   k_count   one workgroup per token tile: one thread per token holds the
+//             token's ids in registers, checks them and counts them into the
+//             tile's expert histogram in LDS, written to tile_counts[tile][E].
 //   k_scan    one workgroup per 64 experts: exclusive scan of tile_counts down
 //             the tiles (in place) and the column totals T[e].
 //   k_solve   one workgroup: home offsets, home load, keep / overflow / deficit
 //             and their prefix sums, then the duplicates as the intersections of
 //             each expert's overflow interval with each rank's deficit interval
 //             (a merge of two sorted boundary lists), and all plan tables.
-//   k_assign  one workgroup per token tile: the stable position of every entry
-//             inside its expert (tile base + per-wave LDS base + in-wave rank from
-//             bit-sliced ballots), then its slot, and the inverse map.
+//   k_assign  one 1024-thread workgroup per token tile: the stable position of
+//             every entry inside its expert (tile base + per-wave base + in-wave
+//             rank from bit-sliced ballots), then its slot -- a home slot, or an
+//             offset into the one duplicate piece of its expert that holds its
+//             overflow index -- and the inverse map.
 //
 // Why this is exact: entry a's position inside expert e is the number of
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
-// waves of this tile) + (earlier lanes of the same 64-entry chunk) + (earlier
-// chunks of this wave), each an integer count taken in entry order.
+// waves of this tile) + (earlier chunks of this wave) + (earlier lanes of the
+// same 64-entry chunk), each an integer count taken in entry order.
 #include "internal.h"
 
 namespace moonep {
 namespace {
 
-constexpr int kWaves = kPlanThreads / 64;
+constexpr int kAssignThreads = 1024;
+constexpr int kAssignWaves = kAssignThreads / 64;
+constexpr int kChunks = kTileEntries / kAssignThreads;  // 64-entry chunks per assign wave
+constexpr int kMaxIdBits = 10;                          // bits of an expert id below kMaxE
+static_assert(kTileEntries % kAssignThreads == 0, "a tile is a whole number of chunks per wave");
+static_assert(kMaxE <= kAssignThreads && kMaxR <= kAssignThreads && kMaxE <= kSolveThreads &&
+                  kMaxR <= kSolveThreads,
+              "one expert or rank per thread (the E-th / R-th prefix entries come from thread 0)");
+static_assert((1 << kMaxIdBits) >= kMaxE, "ids fit the ballot bit slices");
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// Inclusive scan over the 64 lanes of a wave.
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS): shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then lane 15 of a row into the next row
+// and lane 31 into the upper two rows. Lanes with no source get 0 added.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
 }
 
@@ -49,35 +62,37 @@ __device__ __forceinline__ int wave_max(int x) {
     return x;
 }
 
-// Exclusive scan of one value per thread over a 1024-thread workgroup.
-// s_w needs 17 ints. Every thread must call it. Returns the exclusive prefix.
-__device__ int block_excl_scan(int v, int *s_w, int &total) {
+// Exclusive scans of NV values per thread over the 1024-thread workgroup, all
+// in one pass (three barriers). s_w needs (16 + 1) * NV ints. Every thread must
+// call it; tot[i] receives the total of value i.
+template <int NV>
+__device__ void block_excl_scan(const int *v, int *res, int *tot, int *s_w) {
+    constexpr int NW = kSolveThreads / 64;
     const int lane = lane_id(), w = threadIdx.x >> 6;
-    const int inc = wave_incl_scan(v);
-    if (lane == 63) s_w[w] = inc;
-    __syncthreads();
-    if (w == 0) {
-        int t = lane < kSolveThreads / 64 ? s_w[lane] : 0;
-        int ti = wave_incl_scan(t);
-        if (lane < kSolveThreads / 64) s_w[lane] = ti - t;
-        if (lane == kSolveThreads / 64 - 1) s_w[16] = ti;
+    int inc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) inc[i] = wave_incl_scan(v[i]);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s_w[i * NW + w] = inc[i];
     }
     __syncthreads();
-    const int res = inc - v + s_w[w];
-    total = s_w[16];
+    if (w == 0) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int t = lane < NW ? s_w[i * NW + lane] : 0;
+            const int ti = wave_incl_scan(t);
+            if (lane < NW) s_w[i * NW + lane] = ti - t;
+            if (lane == NW - 1) s_w[NV * NW + i] = ti;
+        }
+    }
     __syncthreads();
-    return res;
-}
-
-__device__ int block_max(int v, int *s_w) {
-    const int lane = lane_id(), w = threadIdx.x >> 6;
-    v = wave_max(v);
-    if (lane == 0) s_w[w] = v;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        res[i] = inc[i] - v[i] + s_w[i * NW + w];
+        tot[i] = s_w[NV * NW + i];
+    }
     __syncthreads();
-    int m = s_w[0];
-    for (int i = 1; i < kSolveThreads / 64; ++i) m = max(m, s_w[i]);
-    __syncthreads();
-    return m;
 }
 
 // First index i in [0, n) with a[i] > x (n if none).
@@ -101,32 +116,71 @@ __device__ __forceinline__ int lower_bound(const int *a, int n, int x) {
 }
 
 // ---------------------------------------------------------------- k_count
+// KMAX: a power of two >= K; TPT tokens per thread cover the largest tile any K
+// in (KMAX/2, KMAX] gives. All of a thread's ids are loaded before any is used.
+constexpr int tpt_of(int kmax) {
+    return (kTileEntries / (kmax == 1 ? 1 : kmax / 2 + 1) + kPlanThreads - 1) / kPlanThreads;
+}
+
+template <int KMAX>
 __global__ __launch_bounds__(kPlanThreads) void k_count(const int32_t *__restrict__ ids,
                                                         PlanShape sh,
                                                         int32_t *__restrict__ tile_counts,
                                                         int32_t *__restrict__ tile_status) {
+    constexpr int TPT = tpt_of(KMAX);
     __shared__ int32_t s_hist[kMaxE];
-    __shared__ int32_t s_ids[kTileEntries];
     __shared__ int32_t s_st;
     const int tile = blockIdx.x, tid = threadIdx.x;
+    const int K = sh.K;
     const int tok0 = tile * sh.tile_tokens;
-    const int n = min(sh.tile_tokens, sh.n_tok - tok0) * sh.K;
-    const int32_t *src = ids + (int64_t)tok0 * sh.K;
+    const int ntok = min(sh.tile_tokens, sh.n_tok - tok0);
     for (int e = tid; e < sh.E; e += kPlanThreads) s_hist[e] = 0;
-    for (int i = tid; i < n; i += kPlanThreads) s_ids[i] = src[i];
     if (tid == 0) s_st = 0;
-    __syncthreads();
-    int st = 0;
-    for (int i = tid; i < n; i += kPlanThreads) {
-        const int e = s_ids[i];
-        if (e < 0 || e >= sh.E) {
-            st |= MOONEP_STATUS_BAD_ID;
-            continue;
+
+    // 16-byte loads when a token's ids are whole 16-byte groups (ids is 16-byte aligned)
+    const bool vec = KMAX >= 4 && (K & 3) == 0;
+    int v[TPT][KMAX];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+        const int t = tid + j * kPlanThreads;
+        const int32_t *src = ids + (int64_t)(tok0 + t) * K;
+#pragma unroll
+        for (int k = 0; k < KMAX; k += 4) {
+            if (vec) {
+                int4 q = make_int4(-1, -1, -1, -1);
+                if (t < ntok && k < K) q = *reinterpret_cast<const int4 *>(src + k);
+                v[j][k] = q.x;
+                if (k + 1 < KMAX) v[j][k + 1] = q.y;
+                if (k + 2 < KMAX) v[j][k + 2] = q.z;
+                if (k + 3 < KMAX) v[j][k + 3] = q.w;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4 && k + u < KMAX; ++u)
+                    v[j][k + u] = (t < ntok && k + u < K) ? src[k + u] : -1;
+            }
         }
-        const int k = i % sh.K, base = i - k;
-        for (int k2 = 0; k2 < k; ++k2)
-            if (s_ids[base + k2] == e) st |= MOONEP_STATUS_REPEAT_ID;
-        atomicAdd(&s_hist[e], 1);
+    }
+    __syncthreads();
+
+    int st = 0;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+        const bool tok_ok = tid + j * kPlanThreads < ntok;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int e = v[j][k];
+            if (tok_ok && k < K) {
+                if (e < 0 || e >= sh.E) {
+                    st |= MOONEP_STATUS_BAD_ID;
+                } else {
+                    bool rep = false;
+#pragma unroll
+                    for (int k2 = 0; k2 < k; ++k2) rep |= v[j][k2] == e;
+                    if (rep) st |= MOONEP_STATUS_REPEAT_ID;
+                    atomicAdd(&s_hist[e], 1);
+                }
+            }
+        }
     }
     if (st) atomicOr(&s_st, st);
     __syncthreads();
@@ -184,24 +238,29 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
     __shared__ int s_listE[kMaxE + kMaxR];
     __shared__ int s_keep[kMaxR], s_Dpre[kMaxR + 1], s_dbeg[kMaxR], s_dend[kMaxR];
     __shared__ int s_nzlo[kMaxR], s_ppre[kMaxR + 1];
-    __shared__ int s_w[17];
-    __shared__ int s_status;
+    __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
+    __shared__ int s_status, s_maxT;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = lane_id();
     const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
-    if (tid == 0) s_status = 0;
-    __syncthreads();
-
-    // 1. histogram totals, tile status, maxT, maxvio
     const int Te = tid < E ? p.T[tid] : 0;
     int st = 0;
     for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
+    if (tid == 0) {
+        s_status = 0;
+        s_maxT = 0;
+    }
+    __syncthreads();
+    // 1. tile status bits and maxT (read at the end, after several barriers)
     if (st) atomicOr(&s_status, st);
-    const int maxT = block_max(Te, s_w);
+    {
+        const int m = wave_max(Te);
+        if (lane == 0) atomicMax(&s_maxT, m);
+    }
 
     // 2. home offsets and load. Expert e lives on rank e / G.
-    int totT;
-    const int cum = block_excl_scan(Te, s_w, totT);
+    int cum, totT;
+    block_excl_scan<1>(&Te, &cum, &totT, s_w);
     if (tid < E) s_cum[tid] = cum;
     if (tid == 0) s_cum[E] = totT;
     __syncthreads();
@@ -210,9 +269,9 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         hoff = cum - s_cum[(tid / G) * G];
         p.hoff[tid] = hoff;
     }
-    int Lr = 0, keep = 0, O = 0, D = 0;
+    int keep = 0, O = 0, D = 0;
     if (tid < R) {
-        Lr = s_cum[(tid + 1) * G] - s_cum[tid * G];
+        const int Lr = s_cum[(tid + 1) * G] - s_cum[tid * G];
         keep = min(Lr, SK);
         O = Lr - keep;
         D = SK - keep;
@@ -222,42 +281,35 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         p.D[tid] = D;
         s_keep[tid] = keep;
     }
+    // each expert's overflow: the part of its home list [hoff, hoff + T) at or
+    // beyond S*K; in the global overflow order (home rank, expert, token, k) --
+    // with contiguous homes simply expert order -- it is [ovpre, ovpre + ov)
+    const int ov = tid < E ? max(hoff + Te, SK) - max(hoff, SK) : 0;
 
-    // 3. water-fill prefix sums
-    int totO, totD;
-    const int opre = block_excl_scan(O, s_w, totO);
-    const int dpre = block_excl_scan(D, s_w, totD);
+    // 3. the water-fill prefix sums of O and D, and of ov and (ov > 0), in one pass
+    int v4[4] = {O, D, ov, ov > 0 ? 1 : 0}, pre[4], tot[4];
+    block_excl_scan<4>(v4, pre, tot, s_w);
+    const int totO = tot[0], totD = tot[1], totNZ = tot[3];
     if (tid < R) {
-        p.Opre[tid] = opre;
-        p.Dpre[tid] = dpre;
-        s_Dpre[tid] = dpre;
+        p.Opre[tid] = pre[0];
+        p.Dpre[tid] = pre[1];
+        s_Dpre[tid] = pre[1];
+    }
+    if (tid < E) {
+        s_ovpre[tid] = pre[2];
+        s_nzpre[tid] = pre[3];
+        if (ov > 0) s_ovlist[pre[3]] = tid;
     }
     if (tid == 0) {
         p.Opre[R] = totO;
         p.Dpre[R] = totD;
         s_Dpre[R] = totD;
-    }
-
-    // 4. each expert's overflow interval [ovpre, ovpre + ov) in the global
-    //    overflow order (home rank, expert, token, k) -- with contiguous homes
-    //    that order is simply expert order.
-    int ov = 0;
-    if (tid < E) ov = max(hoff + Te, SK) - max(hoff, SK);
-    int totOV, totNZ;
-    const int ovpre = block_excl_scan(ov, s_w, totOV);
-    const int nzpre = block_excl_scan(ov > 0 ? 1 : 0, s_w, totNZ);
-    if (tid < E) {
-        s_ovpre[tid] = ovpre;
-        s_nzpre[tid] = nzpre;
-        if (ov > 0) s_ovlist[nzpre] = tid;
-    }
-    if (tid == 0) {
-        s_ovpre[E] = totOV;
+        s_ovpre[E] = tot[2];
         s_nzpre[E] = totNZ;
     }
     __syncthreads();
 
-    // 5. pieces per deficit rank: overflowing experts whose interval meets the
+    // 4. pieces per deficit rank: overflowing experts whose interval meets the
     //    rank's filled deficit interval [dbeg, dend).
     int np = 0;
     if (tid < R) {
@@ -271,23 +323,23 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
             s_nzlo[tid] = s_nzpre[elo];
         }
         p.n_dup[tid] = np;
-    }
-    int P, M;
-    const int ppre = block_excl_scan(np, s_w, P);
-    const int mpre = block_excl_scan(tid < R ? min(np, sh.B) : 0, s_w, M);
-    if (tid < R) {
-        s_ppre[tid] = ppre;
-        p.mat_pre[tid] = mpre;
         if (np > sh.B) atomicOr(&s_status, MOONEP_STATUS_OVER_B);
+    }
+    int v2[2] = {np, tid < R ? min(np, sh.B) : 0}, ppre[2], ptot[2];
+    block_excl_scan<2>(v2, ppre, ptot, s_w);
+    const int P = ptot[0];
+    if (tid < R) {
+        s_ppre[tid] = ppre[0];
+        p.mat_pre[tid] = ppre[1];
     }
     if (tid == 0) {
         s_ppre[R] = P;
-        p.mat_pre[R] = M;
+        p.mat_pre[R] = ptot[1];
         p.n_list[0] = P;
     }
     __syncthreads();
 
-    // 6. one thread per piece: rank-major order equals (expert, rank) order
+    // 5. one thread per piece: rank-major order equals (expert, rank) order
     //    because both interval families are increasing.
     const int sp = G + sh.dcap + 1, se = G + sh.dcap;
     for (int q = tid; q < P; q += kSolveThreads) {
@@ -304,17 +356,18 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         p.list_expert[q] = e;
         p.list_rank[q] = r;
         p.list_b[q] = b;
+        p.piece_js[q] = js;
         p.seg_ptr[(int64_t)r * sp + G + b] = start;
         p.seg_expert[(int64_t)r * se + G + b] = e;
         s_listE[q] = e;
     }
     __syncthreads();
 
-    // 7. CSR of the list over experts; experts with duplicates = overflowing experts
+    // 6. CSR of the list over experts; experts with duplicates = overflowing experts
     for (int e = tid; e <= E; e += kSolveThreads) p.dup_ptr[e] = lower_bound(s_listE, P, e);
     for (int i = tid; i < totNZ; i += kSolveThreads) p.xlist[i] = s_ovlist[i];
 
-    // 8. home segments and the end of each rank's filled rows
+    // 7. home segments and the end of each rank's filled rows
     if (tid < E) {
         const int r = tid / G, i = tid - r * G;
         p.seg_ptr[(int64_t)r * sp + i] = min(hoff, SK);
@@ -322,8 +375,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
     }
     if (tid < R) p.seg_ptr[(int64_t)tid * sp + G + np] = keep + (s_dend[tid] - s_dbeg[tid]);
 
-    __syncthreads();
     if (tid == 0) {
+        const int maxT = s_maxT;
         p.n_x[0] = totNZ;
         p.maxT[0] = maxT;
         p.maxvio[0] = (double)((int64_t)maxT * E) / (double)sh.n_ent - 1.0;
@@ -332,74 +385,141 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
 }
 
 // ---------------------------------------------------------------- k_assign
-__global__ __launch_bounds__(kPlanThreads) void k_assign(const int32_t *__restrict__ ids,
-                                                         PlanShape sh, PlanPtrs p) {
-    __shared__ int32_t s_ids[kTileEntries];
-    __shared__ int32_t s_hist[kWaves][kMaxE];
-    __shared__ int32_t s_Dpre[kMaxR + 1], s_Opre[kMaxR + 1], s_keep[kMaxR];
+// Wave w of the tile takes entries [w*256, w*256 + 256) as kChunks chunks of 64,
+// lane l holding entry w*256 + c*64 + l of chunk c.
+// LDS of k_assign, sized to the problem (ints): see the carve-up below.
+inline size_t assign_lds_bytes(const PlanShape &sh) {
+    return sizeof(int32_t) * ((size_t)(kAssignWaves / 2) * sh.E + 3 * (size_t)sh.E + 1 +
+                              2 * (size_t)sh.pcap + 3 * (size_t)sh.R + 2);
+}
+
+// Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
+// compiler budget scalar registers for that (the plan pointers would otherwise
+// hold enough of them to allow only one).
+__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     const int tile = blockIdx.x, tid = threadIdx.x;
     const int lane = lane_id(), w = tid >> 6;
     const int E = sh.E, R = sh.R, SK = sh.SK;
+    extern __shared__ int32_t smem[];
+    // Per-wave counts, then running positions relative to the tile's base, of
+    // waves 2m (low 16 bits) and 2m+1 (high 16 bits) of every expert: s_pos[m*E + e].
+    // A tile has at most 4096 entries, so a half never carries into the other.
+    uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
+    int32_t *s_tbase = smem + (kAssignWaves / 2) * E;  // earlier tiles + home offset
+    int32_t *s_home = s_tbase + E;                      // home rank of each expert
+    int32_t *s_dup_ptr = s_home + E;                    // pieces of e: [s_dup_ptr[e], [e+1])
+    int32_t *s_pjs = s_dup_ptr + E + 1;                 // first overflow index of each piece
+    int32_t *s_pslot = s_pjs + sh.pcap;                 // first global slot of each piece
+    int32_t *s_Opre = s_pslot + sh.pcap;                // R + 1
+    int32_t *s_Dpre = s_Opre + R + 1;                   // R + 1
+    int32_t *s_keep = s_Dpre + R + 1;                   // R
     const int tok0 = tile * sh.tile_tokens;
     const int n = min(sh.tile_tokens, sh.n_tok - tok0) * sh.K;
     const int64_t a0 = (int64_t)tok0 * sh.K;
+    const int P = p.n_list[0];
 
-    for (int i = tid; i < n; i += kPlanThreads) s_ids[i] = ids[a0 + i];
-    for (int i = tid; i < kWaves * E; i += kPlanThreads) s_hist[i / E][i % E] = 0;
-    for (int r = tid; r <= R; r += kPlanThreads) {
-        s_Dpre[r] = p.Dpre[r];
-        s_Opre[r] = p.Opre[r];
-        if (r < R) s_keep[r] = p.keep[r];
+    // loads first, all in flight: this wave's ids, then one table element per thread
+    int idv[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int i = w * (kChunks * 64) + c * 64 + lane;
+        idv[c] = i < n ? ids[a0 + i] : -1;
     }
-    __syncthreads();
-
-    // each wave owns a contiguous run of whole 64-entry chunks of the tile
-    const int per = ((n + kWaves - 1) / kWaves + 63) & ~63;
-    const int beg = min(w * per, n), end = min(beg + per, n);
-
-    // pass 1: per-wave expert counts
-    for (int i = beg + lane; i < end; i += 64) {
-        const int e = s_ids[i];
-        if (e >= 0 && e < E) atomicAdd(&s_hist[w][e], 1);
+    int gbase = 0;
+    if (tid < E) {
+        gbase = p.tile_counts[(int64_t)tile * E + tid] + p.hoff[tid];
+        s_home[tid] = tid / sh.G;
     }
-    __syncthreads();
-    // per-wave bases: earlier tiles + home offset + earlier waves of this tile
-    const int32_t *tbase = p.tile_counts + (int64_t)tile * E;
-    for (int e = tid; e < E; e += kPlanThreads) {
-        int base = tbase[e] + p.hoff[e];
-        for (int v = 0; v < kWaves; ++v) {
-            const int c = s_hist[v][e];
-            s_hist[v][e] = base;
-            base += c;
-        }
+    if (tid < E) s_dup_ptr[tid] = p.dup_ptr[tid];
+    if (tid < R) {
+        s_Opre[tid] = p.Opre[tid];
+        s_Dpre[tid] = p.Dpre[tid];
+        s_keep[tid] = p.keep[tid];
     }
+    if (tid == 0) {
+        s_dup_ptr[E] = p.dup_ptr[E];
+        s_Opre[R] = p.Opre[R];
+        s_Dpre[R] = p.Dpre[R];
+    }
+    for (int q = tid; q < P; q += kAssignThreads) {
+        const int r = p.list_rank[q];
+        s_pjs[q] = p.piece_js[q];
+        s_pslot[q] = r * SK + p.dup_start[(int64_t)r * sh.dcap + p.list_b[q]];
+    }
+#pragma unroll
+    for (int m = 0; m < kAssignWaves / 2; ++m)
+        if (tid < E) s_pos[m * E + tid] = 0u;
     __syncthreads();
+    const int half = (w & 1) * 16;
 
-    // pass 2: chunks of 64 entries in order; rank among equal ids of the chunk
-    for (int c0 = beg; c0 < end; c0 += 64) {
-        const int i = c0 + lane;
-        const int e = i < end ? s_ids[i] : -1;
+    // pass 1: which lanes of each chunk hold the same id (bit-sliced ballots);
+    // the lowest lane of each group adds the group's size to the wave's count
+    uint64_t same[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int e = idv[c];
         const bool valid = e >= 0 && e < E;
         uint64_t mask = __ballot(valid);
-        for (int bit = 0; bit < sh.id_bits; ++bit) {
-            const bool set = valid && ((e >> bit) & 1);
-            const uint64_t bb = __ballot(set);
-            mask &= set ? bb : ~bb;
+#pragma unroll
+        for (int bit = 0; bit < kMaxIdBits; ++bit) {
+            if (bit < sh.id_bits) {
+                const bool set = valid && ((e >> bit) & 1);
+                const uint64_t bb = __ballot(set);
+                mask &= set ? bb : ~bb;
+            }
         }
+        same[c] = mask;
+        if (valid && lane == __ffsll((unsigned long long)mask) - 1)
+            atomicAdd(&s_pos[(w >> 1) * E + e], (uint32_t)__popcll(mask) << half);
+    }
+    __syncthreads();
+    // running positions: earlier waves of this tile, relative to the tile base
+    // (earlier tiles + home offset)
+    if (tid < E) {
+        uint32_t run = 0;
+#pragma unroll
+        for (int m = 0; m < kAssignWaves / 2; ++m) {
+            const uint32_t word = s_pos[m * E + tid];
+            const uint32_t lo = word & 0xffffu, hi = word >> 16;
+            s_pos[m * E + tid] = run | ((run + lo) << 16);
+            run += lo + hi;
+        }
+        s_tbase[tid] = gbase;
+    }
+    __syncthreads();
+
+    // pass 2: chunks in order; position = wave's running position + lanes below
+    // with the same id; then the slot
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int e = idv[c];
+        const int i = w * (kChunks * 64) + c * 64 + lane;
+        const bool valid = e >= 0 && e < E;
         if (valid) {
+            const uint64_t mask = same[c];
             const int below = __builtin_amdgcn_mbcnt_hi(
                 (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-            const int base = s_hist[w][e];
-            const int h = base + below;
-            if (lane == 63 - __clzll((long long)mask)) s_hist[w][e] = base + __popcll(mask);
-            const int r = e / sh.G;
-            int slot;
+            const int rel = (int)((s_pos[(w >> 1) * E + e] >> half) & 0xffffu);
+            const int h = s_tbase[e] + rel + below;
+            // the wave's read above is issued before this add (LDS keeps a wave's
+            // operations in order); the other wave of the word only adds to its half
+            if (lane == 63 - __clzll((long long)mask))
+                atomicAdd(&s_pos[(w >> 1) * E + e], (uint32_t)__popcll(mask) << half);
+            const int r = s_home[e];
+            int slot = -1;
             if (h < SK) {
                 slot = r * SK + h;
             } else {
+                // overflow index j lies in exactly one piece of expert e; the pieces
+                // of an expert are in increasing j
                 const int j = s_Opre[r] + (h - SK);
-                const int r2 = min(upper_bound(s_Dpre, R + 1, j) - 1, R - 1);
-                slot = r2 * SK + s_keep[r2] + (j - s_Dpre[r2]);
+                int q = s_dup_ptr[e];
+                const int q1 = s_dup_ptr[e + 1];
+                if (q < q1) {
+                    while (q + 1 < q1 && j >= s_pjs[q + 1]) ++q;
+                    slot = s_pslot[q] + (j - s_pjs[q]);
+                }
             }
             // A correct plan always lands inside the buffer; the guard only keeps a
             // broken invariant from turning into a wild store.
@@ -409,18 +529,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_assign(const int32_t *__restri
             } else {
                 p.dst[a0 + i] = -1;
             }
-        } else if (i < end) {
+        } else if (i < n) {
             p.dst[a0 + i] = -1;
         }
     }
 
     // Tails of the plan tables and unfilled slots, spread over the whole grid.
-    const int64_t gt = (int64_t)blockIdx.x * kPlanThreads + tid;
-    const int64_t gn = (int64_t)gridDim.x * kPlanThreads;
+    const int gt = blockIdx.x * kAssignThreads + tid;
+    const int gn = gridDim.x * kAssignThreads;
     const int sp = sh.G + sh.dcap + 1, se = sh.G + sh.dcap;
-    const int64_t ntab = (int64_t)R * sh.dcap;
-    for (int64_t x = gt; x < ntab; x += gn) {
-        const int r = (int)(x / sh.dcap), j = (int)(x - (int64_t)r * sh.dcap);
+    const int ntab = R * sh.dcap;  // < 2^31: R, dcap <= 1024
+    for (int x = gt; x < ntab; x += gn) {
+        const int r = x / sh.dcap, j = x - r * sh.dcap;
         if (j >= p.n_dup[r]) {
             p.dup_expert[x] = -1;
             p.dup_start[x] = -1;
@@ -429,16 +549,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_assign(const int32_t *__restri
             p.seg_expert[(int64_t)r * se + sh.G + j] = -1;
         }
     }
-    const int P = p.n_list[0];
-    for (int64_t x = P + gt; x < sh.pcap; x += gn) {
+    for (int x = P + gt; x < sh.pcap; x += gn) {
         p.list_expert[x] = -1;
         p.list_rank[x] = -1;
         p.list_b[x] = -1;
+        p.piece_js[x] = -1;
     }
     // slots that receive nothing (only when some ids were dropped)
     const int totO = s_Opre[R], totD = s_Dpre[R];
-    for (int64_t j = totO + gt; j < totD; j += gn) {
-        const int r2 = upper_bound(s_Dpre, R + 1, (int)j) - 1;
+    for (int j = totO + gt; j < totD; j += gn) {
+        const int r2 = upper_bound(s_Dpre, R + 1, j) - 1;
         p.src[(int64_t)r2 * SK + s_keep[r2] + (j - s_Dpre[r2])] = -1;
     }
 }
@@ -447,12 +567,28 @@ __global__ __launch_bounds__(kPlanThreads) void k_assign(const int32_t *__restri
 
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p,
                        hipStream_t st) {
-    hipLaunchKernelGGL(k_count, dim3(sh.n_tiles), dim3(kPlanThreads), 0, st, ids, sh,
-                       p.tile_counts, p.tile_status);
+    const dim3 tiles(sh.n_tiles);
+#define MOONEP_COUNT(KM)                                                                    \
+    hipLaunchKernelGGL(k_count<KM>, tiles, dim3(kPlanThreads), 0, st, ids, sh, p.tile_counts, \
+                       p.tile_status)
+    if (sh.K <= 1) MOONEP_COUNT(1);
+    else if (sh.K <= 2) MOONEP_COUNT(2);
+    else if (sh.K <= 4) MOONEP_COUNT(4);
+    else if (sh.K <= 8) MOONEP_COUNT(8);
+    else if (sh.K <= 16) MOONEP_COUNT(16);
+    else if (sh.K <= 32) MOONEP_COUNT(32);
+    else MOONEP_COUNT(64);
+#undef MOONEP_COUNT
     hipLaunchKernelGGL(k_scan, dim3((sh.E + 63) / 64), dim3(kScanThreads), 0, st, sh,
                        p.tile_counts, p.T);
     hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
-    hipLaunchKernelGGL(k_assign, dim3(sh.n_tiles), dim3(kPlanThreads), 0, st, ids, sh, p);
+    const size_t lds = assign_lds_bytes(sh);
+    if (lds > 65536) {  // beyond the default dynamic LDS limit of a launch
+        const hipError_t e = hipFuncSetAttribute((const void *)k_assign,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_assign, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
     return hipGetLastError();
 }
 
