@@ -15,6 +15,10 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   combine   -- pinned: closed forms, binary64 error bound, library bf16 rounding
   reduce    -- pinned: hand-derived rounding-order value, integer closed form,
                binary64 error bound
+  plan(bounded=True)
+            -- pinned: hand-worked examples, invariants of any balanced plan plus
+               the B bound, brute-force minimality of the overflowing experts,
+               closed forms (balanced input, one overloaded rank)
   combine_backward_y, combine_backward_w, dispatch_backward
             -- pinned: torch autograd in binary64 of the plain forward
                definitions (gather, weighted sum), torch's bf16 rounding, closed
@@ -71,6 +75,8 @@ def _load() -> ctypes.CDLL:
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_plan.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, _P(_PlanOut)]
         lib.oracle_plan.restype = ctypes.c_int
+        lib.oracle_plan_bounded.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, _P(_PlanOut)]
+        lib.oracle_plan_bounded.restype = ctypes.c_int
         lib.oracle_dispatch.argtypes = [i64, i32, i64, vp, vp, i64, i64, vp]
         lib.oracle_dispatch.restype = None
         lib.oracle_replicate.argtypes = [i32, i32, i32, vp, vp, i64, vp, vp]
@@ -107,8 +113,11 @@ def pcap_of(R: int, E: int) -> int:
     return E + R
 
 
-def plan(R: int, E: int, K: int, S: int, B: int, ids: np.ndarray) -> Dict[str, np.ndarray]:
-    """The water-fill plan of one step's router ids [R,S,K] (see moonep_oracle.c)."""
+def plan(R: int, E: int, K: int, S: int, B: int, ids: np.ndarray,
+         bounded: bool = False) -> Dict[str, np.ndarray]:
+    """The water-fill plan of one step's router ids [R,S,K] (see moonep_oracle.c);
+    bounded=True gives the plan that keeps at most B duplicates per rank where it
+    can (oracle_plan_bounded)."""
     lib = _load()
     ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
     if ids.size != R * S * K:
@@ -132,7 +141,8 @@ def plan(R: int, E: int, K: int, S: int, B: int, ids: np.ndarray) -> Dict[str, n
     po = _PlanOut()
     for name, ctype in _PlanOut._fields_:
         setattr(po, name, ctypes.cast(out[name].ctypes.data, ctype))
-    rc = lib.oracle_plan(R, E, K, S, B, _ptr(ids), dcap, pcap, ctypes.byref(po))
+    fn = lib.oracle_plan_bounded if bounded else lib.oracle_plan
+    rc = fn(R, E, K, S, B, _ptr(ids), dcap, pcap, ctypes.byref(po))
     if rc != 0:
         raise ValueError("oracle_plan rejected its arguments")
     out["dcap"], out["pcap"] = dcap, pcap

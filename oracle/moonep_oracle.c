@@ -385,3 +385,227 @@ void oracle_dispatch_backward(int64_t n_tok, int32_t K, int64_t H, int32_t in_dt
             store_elem(grad_hidden, out_dtype, g * H + i, acc);
         }
 }
+
+/* ---------------------------------------------------------------- bounded plan
+ * A plan for inference, where each rank should hold at most B duplicate experts
+ * (news.hamidun.com EN, "Key facts about the release": B = 3-4 for inference).
+ * The pages do not say how the bound is met; this is the reading used here. It
+ * keeps exact S*K rows per rank and the same (minimum) number of moved rows as
+ * the water-fill, and changes two choices:
+ *   1. which home rows overflow: an overloaded rank overflows its largest
+ *      experts first (home experts ordered by T descending, then id), so the
+ *      same O_r rows leave through as few experts as possible; inside an expert
+ *      the kept rows are its first (token, k) entries and the overflow its last;
+ *   2. where the overflow goes: deficit ranks are filled one at a time, in order
+ *      of deficit D descending (then rank id); a rank's pieces 1 .. B-1 are whole
+ *      items -- the largest remaining overflow that fits (then lowest expert id),
+ *      or, if none fits, a piece of the largest remaining overflow that fills the
+ *      rank; its B-th piece is a piece of the smallest remaining overflow that is
+ *      at least the rank's free room (then lowest expert id), which fills it, or
+ *      if no overflow is that large, the largest remaining one whole. A rank
+ *      that still has room after B pieces goes on the same way and
+ *      ST_OVER_B is raised.
+ * Rows of a rank: home experts in id order (kept rows only), then its pieces in
+ * the order they were placed. Every other table has the water-fill's meaning.
+ */
+int oracle_plan_bounded(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
+                        const int32_t *ids, int32_t dcap, int32_t pcap, oracle_plan_out *o)
+{
+    if (R <= 0 || E <= 0 || K <= 0 || S <= 0 || B < 0 || E % R != 0 || K > E) return -1;
+    const int64_t G = E / R, SK = (int64_t)S * K, N = (int64_t)R * S, NE = N * K;
+    int32_t status = 0;
+
+    /* validate, histogram, maxvio, home offsets and the water-fill quantities:
+       exactly as in oracle_plan */
+    for (int64_t g = 0; g < N; ++g)
+        for (int k = 0; k < K; ++k) {
+            int32_t e = ids[g * K + k];
+            if (e < 0 || e >= E) { status |= ST_BAD_ID; continue; }
+            for (int k2 = 0; k2 < k; ++k2)
+                if (ids[g * K + k2] == e) status |= ST_REPEAT_ID;
+        }
+    for (int e = 0; e < E; ++e) o->T[e] = 0;
+    for (int64_t a = 0; a < NE; ++a)
+        if (ids[a] >= 0 && ids[a] < E) o->T[ids[a]] += 1;
+    int64_t maxT = 0;
+    for (int e = 0; e < E; ++e) if (o->T[e] > maxT) maxT = o->T[e];
+    *o->maxT = maxT;
+    *o->maxvio = (double)(maxT * (int64_t)E) / (double)NE - 1.0;
+    for (int r = 0; r < R; ++r) {
+        int64_t acc = 0;
+        for (int64_t i = 0; i < G; ++i) {
+            o->hoff[r * G + i] = (int32_t)acc;
+            acc += o->T[r * G + i];
+        }
+        o->L[r] = (int32_t)acc;
+    }
+    o->Opre[0] = 0;
+    o->Dpre[0] = 0;
+    for (int r = 0; r < R; ++r) {
+        o->keep[r] = o->L[r] < SK ? o->L[r] : (int32_t)SK;
+        o->O[r] = o->L[r] - o->keep[r];
+        o->D[r] = (int32_t)SK - o->keep[r];
+        o->Opre[r + 1] = o->Opre[r] + o->O[r];
+        o->Dpre[r + 1] = o->Dpre[r] + o->D[r];
+    }
+
+    int64_t *ov = (int64_t *)calloc((size_t)E, sizeof(int64_t));    /* overflow rows   */
+    int64_t *left = (int64_t *)calloc((size_t)E, sizeof(int64_t));  /* not yet placed  */
+    int64_t *koff = (int64_t *)calloc((size_t)E, sizeof(int64_t));  /* home slot start */
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *taken = (int32_t *)calloc((size_t)G, sizeof(int32_t));
+    /* pieces in placement order */
+    int32_t *pe = (int32_t *)malloc(sizeof(int32_t) * (size_t)(pcap > 0 ? pcap : 1));
+    int32_t *pr = (int32_t *)malloc(sizeof(int32_t) * (size_t)(pcap > 0 ? pcap : 1));
+    int64_t *pstart = (int64_t *)malloc(sizeof(int64_t) * (size_t)(pcap > 0 ? pcap : 1));
+    int64_t *pcount = (int64_t *)malloc(sizeof(int64_t) * (size_t)(pcap > 0 ? pcap : 1));
+    int64_t *pfirst = (int64_t *)malloc(sizeof(int64_t) * (size_t)(pcap > 0 ? pcap : 1));
+    int32_t *rdone = (int32_t *)calloc((size_t)R, sizeof(int32_t));
+    int rc = -1;
+    if (!ov || !left || !koff || !seen || !taken || !pe || !pr || !pstart || !pcount || !pfirst || !rdone)
+        goto out;
+
+    /* 1. overflow of each overloaded rank, from its largest experts */
+    for (int r = 0; r < R; ++r) {
+        int64_t rem = o->O[r];
+        for (int64_t i = 0; i < G; ++i) taken[i] = 0;
+        while (rem > 0) {
+            int64_t best = -1;
+            for (int64_t i = 0; i < G; ++i)
+                if (!taken[i] && (best < 0 || o->T[r * G + i] > o->T[r * G + best])) best = i;
+            if (best < 0) goto out;
+            taken[best] = 1;
+            int64_t e = r * G + best;
+            int64_t t = o->T[e] < rem ? o->T[e] : rem;
+            ov[e] = t;
+            rem -= t;
+        }
+        int64_t acc = 0;  /* kept rows in id order */
+        for (int64_t i = 0; i < G; ++i) {
+            koff[r * G + i] = acc;
+            acc += o->T[r * G + i] - ov[r * G + i];
+        }
+    }
+    for (int e = 0; e < E; ++e) left[e] = ov[e];
+
+    /* 2. fill the deficit ranks, largest deficit first */
+    int32_t np = 0;
+    for (int step = 0; step < R; ++step) {
+        int r = -1;
+        for (int q = 0; q < R; ++q)
+            if (!rdone[q] && o->D[q] > 0 && (r < 0 || o->D[q] > o->D[r])) r = q;
+        if (r < 0) break;
+        rdone[r] = 1;
+        int64_t room = o->D[r];
+        int32_t used = 0;
+        while (room > 0) {
+            int e = -1;
+            if (used < B - 1) {
+                /* largest overflow that fits whole, else the largest (split) */
+                for (int x = 0; x < E; ++x)
+                    if (left[x] > 0 && left[x] <= room && (e < 0 || left[x] > left[e])) e = x;
+                if (e < 0)
+                    for (int x = 0; x < E; ++x)
+                        if (left[x] > 0 && (e < 0 || left[x] > left[e])) e = x;
+            } else {
+                /* smallest overflow that fills the room, else the largest */
+                for (int x = 0; x < E; ++x)
+                    if (left[x] >= room && (e < 0 || left[x] < left[e])) e = x;
+                if (e < 0)
+                    for (int x = 0; x < E; ++x)
+                        if (left[x] > 0 && (e < 0 || left[x] > left[e])) e = x;
+            }
+            if (e < 0) break;  /* nothing left to place (only when ids were dropped) */
+            if (np >= pcap) goto out;
+            int64_t t = left[e] < room ? left[e] : room;
+            pe[np] = e;
+            pr[np] = r;
+            pstart[np] = o->keep[r] + (o->D[r] - room);
+            pcount[np] = t;
+            pfirst[np] = ov[e] - left[e];
+            ++np;
+            left[e] -= t;
+            room -= t;
+            ++used;
+        }
+    }
+
+    /* 3. place every entry: kept rows at home, overflow rows in their piece */
+    for (int64_t s = 0; s < NE; ++s) o->src[s] = -1;
+    for (int64_t a = 0; a < NE; ++a) {
+        int32_t e = ids[a];
+        if (e < 0 || e >= E) { o->dst[a] = -1; continue; }
+        int64_t r = e / G, h = seen[e]++;
+        int64_t kept = o->T[e] - ov[e];
+        int64_t slot = -1;
+        if (h < kept) {
+            slot = r * SK + koff[e] + h;
+        } else {
+            int64_t j = h - kept;
+            for (int32_t q = 0; q < np; ++q)
+                if (pe[q] == e && pfirst[q] <= j && j < pfirst[q] + pcount[q])
+                    slot = pr[q] * SK + pstart[q] + (j - pfirst[q]);
+        }
+        if (slot < 0) goto out;
+        o->dst[a] = (int32_t)slot;
+        o->src[slot] = (int32_t)a;
+    }
+
+    /* 4. duplicate tables (pieces of each rank in placement order), segments,
+          and the global list ordered by (expert, rank) */
+    for (int64_t i = 0; i < (int64_t)R * dcap; ++i) {
+        o->dup_expert[i] = -1;
+        o->dup_start[i] = -1;
+        o->dup_count[i] = 0;
+    }
+    const int64_t sp = G + dcap + 1, se = G + dcap;
+    for (int r = 0; r < R; ++r) {
+        int32_t b = 0;
+        int64_t end = o->keep[r];
+        for (int64_t i = 0; i < sp; ++i) o->seg_ptr[r * sp + i] = -1;
+        for (int64_t i = 0; i < se; ++i) o->seg_expert[r * se + i] = -1;
+        for (int64_t i = 0; i < G; ++i) {
+            o->seg_ptr[r * sp + i] = (int32_t)koff[r * G + i];
+            o->seg_expert[r * se + i] = (int32_t)(r * G + i);
+        }
+        for (int32_t q = 0; q < np; ++q) {
+            if (pr[q] != r) continue;
+            if (b >= dcap) goto out;
+            o->dup_expert[(int64_t)r * dcap + b] = pe[q];
+            o->dup_start[(int64_t)r * dcap + b] = (int32_t)pstart[q];
+            o->dup_count[(int64_t)r * dcap + b] = (int32_t)pcount[q];
+            o->seg_ptr[r * sp + G + b] = (int32_t)pstart[q];
+            o->seg_expert[r * se + G + b] = pe[q];
+            end = pstart[q] + pcount[q];
+            ++b;
+        }
+        o->seg_ptr[r * sp + G + b] = (int32_t)end;
+        o->n_dup[r] = b;
+        if (b > B) status |= ST_OVER_B;
+    }
+    for (int32_t p = 0; p < pcap; ++p) {
+        o->list_expert[p] = -1;
+        o->list_rank[p] = -1;
+        o->list_b[p] = -1;
+    }
+    int32_t p = 0;
+    for (int e = 0; e < E; ++e) {
+        o->dup_ptr[e] = p;
+        for (int r = 0; r < R; ++r)
+            for (int b = 0; b < o->n_dup[r]; ++b)
+                if (o->dup_expert[(int64_t)r * dcap + b] == e) {
+                    o->list_expert[p] = e;
+                    o->list_rank[p] = r;
+                    o->list_b[p] = b;
+                    ++p;
+                }
+    }
+    o->dup_ptr[E] = p;
+    *o->n_list = p;
+    *o->status = status;
+    rc = 0;
+out:
+    free(ov); free(left); free(koff); free(seen); free(taken);
+    free(pe); free(pr); free(pstart); free(pcount); free(pfirst); free(rdone);
+    return rc;
+}
