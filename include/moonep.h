@@ -119,6 +119,7 @@ typedef struct moonep_layout {
     int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
     int64_t n_list, list_expert, list_rank, list_b, dup_ptr;
     int64_t ws_tile_counts, ws_tile_status, ws_mat_pre, ws_xlist, ws_n_x, ws_piece_js;
+    int64_t ws_kept, ws_koff, ws_upre;
 } moonep_layout;
 
 /* Fills *out for dims. Pure host computation. Returns MOONEP_OK or
@@ -143,6 +144,34 @@ int moonep_plan_layout(const moonep_dims *dims, moonep_layout *out);
  * bit-for-bit deterministic.
  */
 int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf, void *stream);
+
+/*
+ * moonep_plan_bounded -- the same plan with at most B duplicates per rank where
+ * the routing allows it, for inference budgets of a few duplicate slots per rank
+ * (news.hamidun.com EN, "Key facts about the release": B of 3 to 4 for
+ * inference; the pages do not say how the budget is met, so the method below is
+ * this library's).
+ *
+ *   arguments, outputs and their layout as moonep_plan
+ *
+ * T, maxvio, L, keep, O, D and the S*K rows per rank are those of moonep_plan;
+ * only which rows leave home, and where they go, differ:
+ *   - an overloaded rank overflows its experts in (T descending, id) order, all
+ *     but the last whole, and every expert keeps its first entries (token, k
+ *     order) at home, packed in expert order from row 0;
+ *   - deficit ranks are filled one at a time, in (D descending, rank) order;
+ *     before a rank's B-th duplicate it takes the largest remaining overflow that
+ *     fits whole (ties: lowest expert id), else a piece of the largest; its B-th
+ *     and later duplicates take the smallest remaining overflow that fills the
+ *     rest (ties: lowest id), else the largest whole;
+ *   - a rank's duplicates are numbered in the order it takes them; the list is
+ *     ordered by (expert, rank).
+ * A rank that still needs more than B duplicates sets MOONEP_STATUS_OVER_B, as in
+ * moonep_plan. Bit-for-bit deterministic; the moves and backward entry points
+ * take its plan unchanged.
+ */
+int moonep_plan_bounded(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf,
+                        void *stream);
 
 /*
  * moonep_dispatch -- zero-copy scatter of token rows into the static,

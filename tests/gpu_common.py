@@ -18,12 +18,12 @@ def dims_for(td, R, E, K, S, B, H, dtype):
     return td.Dims(R, E, K, S, B, dtype, H)
 
 
-def run_plan(td, dims, ids_np, dev, plan_buf=None):
+def run_plan(td, dims, ids_np, dev, plan_buf=None, bounded=False):
     import torch
     if plan_buf is None:
         plan_buf = td.new_plan_buffer(dims, dev)
     ids_d = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
-    td.moonep_plan(dims, ids_d, plan_buf)
+    (td.moonep_plan_bounded if bounded else td.moonep_plan)(dims, ids_d, plan_buf)
     torch.cuda.synchronize()
     return plan_buf, ids_d
 

@@ -5,6 +5,9 @@ reduce accumulate in binary32 in the same fixed order as the oracle, so they are
 compared bit for bit too, which is stricter than the 1e-5 relative bound the
 path promises (that bound is also asserted on the fp32 combine output).
 
+Both plans are covered: the water-fill (moonep_plan) and the plan bounded by B
+duplicates per rank (moonep_plan_bounded), each against its oracle.
+
 Small shapes are compared element by element; they span several plan tiles with
 a ragged last tile and rows whose 16-byte chunk count does not fill the lanes.
 The five workload shapes are run at full size in the launch configuration the
@@ -76,13 +79,13 @@ def _host_rows(t):
     return t.detach().contiguous().cpu().numpy()
 
 
-def _full_case(td, wl, ids, w, seed):
+def _full_case(td, wl, ids, w, seed, bounded=False):
     """Everything compared element by element (small shapes only)."""
     dims = _dims(td, wl)
-    say(f"case {wl.name}: {dims}")
-    plan_buf, _ = run_plan(td, dims, ids, DEV)
+    say(f"case {wl.name} bounded={bounded}: {dims}")
+    plan_buf, _ = run_plan(td, dims, ids, DEV, bounded=bounded)
     g = read_plan(td, dims, plan_buf)
-    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
     assert_plan_equal(g, p)
     valid = bool(np.all((ids >= 0) & (ids < wl.E)))
     check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g, valid_input=valid)
@@ -136,10 +139,11 @@ def _full_case(td, wl, ids, w, seed):
     return g
 
 
+@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_small_shapes_elementwise(td, wl):
+def test_small_shapes_elementwise(td, wl, bounded):
     ids, w = W.make_routing(wl, seed=3)
-    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3)
+    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
 
 
 def test_hand_worked_examples_on_gpu(td):
@@ -162,7 +166,40 @@ def test_hand_worked_examples_on_gpu(td):
         assert_plan_equal(g, oracle.plan(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], ids))
 
 
-def test_invalid_and_repeated_ids(td):
+def test_bounded_hand_worked_examples_on_gpu(td):
+    import glob
+    import json
+    import os
+    paths = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden",
+                                          "bounded_example*.json")))
+    assert paths
+    for path in paths:
+        ex = json.load(open(path))
+        R, E, K, S, B = ex["R"], ex["E"], ex["K"], ex["S"], ex["B"]
+        dims = td.Dims(R, E, K, S, B, W.F32, 4)
+        say(f"golden {os.path.basename(path)}")
+        ids = np.array(ex["ids"], np.int32)
+        plan_buf, _ = run_plan(td, dims, ids, DEV, bounded=True)
+        g = read_plan(td, dims, plan_buf)
+        SK, G = S * K, E // R
+        x = ex["expect"]
+        assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
+        assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
+        assert float(g["maxvio"][0]) == x["maxvio"]
+        got_dups = [[r, b, int(g["dup_expert"][r, b]), int(g["dup_start"][r, b]),
+                     int(g["dup_count"][r, b])] for r in range(R) for b in range(int(g["n_dup"][r]))]
+        assert got_dups == x["dups"]
+        nl = int(g["n_list"][0])
+        assert [[int(g["list_expert"][i]), int(g["list_rank"][i]), int(g["list_b"][i])]
+                for i in range(nl)] == x["list"]
+        for r in range(R):
+            ns = G + int(g["n_dup"][r])
+            assert g["seg_ptr"][r, :ns + 1].tolist() == x["seg_ptr"][r]
+        assert_plan_equal(g, oracle.plan(R, E, K, S, B, ids, bounded=True))
+
+
+@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
+def test_invalid_and_repeated_ids(td, bounded):
     wl = _wl("bad_ids", 4, 32, 4, 1500, 4, 64, W.BF16, 2.0)
     rng = np.random.default_rng(17)
     ids, w = W.make_routing(wl, seed=5)
@@ -170,28 +207,29 @@ def test_invalid_and_repeated_ids(td):
     w = w.reshape(-1)
     bad = rng.choice(ids.size, 40, replace=False)
     ids[bad] = rng.choice([-1, -100, wl.E, wl.E + 7], 40)
-    g = _full_case(td, wl, ids, w, 5)
+    g = _full_case(td, wl, ids, w, 5, bounded)
     assert int(g["status"][0]) & 1
     ids2, w2 = W.make_routing(wl, seed=6)
     ids2 = ids2.reshape(-1, wl.K).copy()
     t = rng.choice(wl.n_tok, 25, replace=False)
     ids2[t, 2] = ids2[t, 0]
-    g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6)
+    g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6, bounded)
     assert int(g["status"][0]) & 2
 
 
-def test_extreme_skew_and_balance(td):
+@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
+def test_extreme_skew_and_balance(td, bounded):
     # every token picks the same K experts, all homed on rank 0
     wl = _wl("one_hot_rank", 8, 64, 8, 1000, 8, 64, W.BF16, 0.0)
     ids = np.tile(np.arange(8, dtype=np.int32), wl.n_tok)
     w = np.full(ids.size, 1.0 / 8, np.float32)
-    g = _full_case(td, wl, ids, w, 1)
+    g = _full_case(td, wl, ids, w, 1, bounded)
     assert int(g["n_dup"].sum()) > 0 and int(g["L"][0]) == wl.n_ent
     # perfectly balanced routing: no overflow, no duplicates
     wl = _wl("balanced", 4, 16, 4, 256, 2, 64, W.BF16, 0.0)
     ids = (np.arange(wl.n_ent) % wl.E).astype(np.int32)
     w = np.full(ids.size, 0.25, np.float32)
-    g = _full_case(td, wl, ids, w, 2)
+    g = _full_case(td, wl, ids, w, 2, bounded)
     assert int(g["n_dup"].sum()) == 0 and float(g["maxvio"][0]) == 0.0
 
 
@@ -247,17 +285,18 @@ def test_plan_buffer_reuse_across_shapes(td):
 
 # ------------------------------------------------------------ full-size shapes
 
+@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
 @pytest.mark.parametrize("name", ["tiny", "uniform", "zipf", "k3", "decode"])
-def test_workload_plans_all_seeds(td, name):
+def test_workload_plans_all_seeds(td, name, bounded):
     wl = W.WORKLOADS[name]
     dims = _dims(td, wl)
     pb = td.new_plan_buffer(dims, DEV)
     for seed in (0, 1, 2):
-        say(f"plan {name} seed {seed}")
+        say(f"plan {name} seed {seed} bounded={bounded}")
         ids, _ = W.make_routing(wl, seed)
-        run_plan(td, dims, ids, DEV, pb)
+        run_plan(td, dims, ids, DEV, pb, bounded=bounded)
         g = read_plan(td, dims, pb)
-        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
         assert_plan_equal(g, p)
         if seed == 0:
             check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g)
@@ -267,15 +306,16 @@ def test_workload_plans_all_seeds(td, name):
             f"(B={wl.B})  total dups {int(g['n_dup'].sum())}  status {int(g['status'][0])}")
 
 
-@pytest.mark.parametrize("name", ["uniform", "zipf", "k3", "decode"])
-def test_workload_data_moves_full_size(td, name):
+@pytest.mark.parametrize("name,bounded", [("uniform", False), ("zipf", False), ("k3", False),
+                                          ("decode", False), ("k3", True), ("decode", True)])
+def test_workload_data_moves_full_size(td, name, bounded):
     wl = W.WORKLOADS[name]
     dims = _dims(td, wl)
     seed = 0
-    say(f"full-size moves {name}: {dims}")
+    say(f"full-size moves {name} bounded={bounded}: {dims}")
     ids, w = W.make_routing(wl, seed)
-    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
-    pb, _ = run_plan(td, dims, ids, DEV)
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
+    pb, _ = run_plan(td, dims, ids, DEV, bounded=bounded)
     assert_plan_equal(read_plan(td, dims, pb), p)
     src_d = torch.from_numpy(p["src"].astype(np.int64)).to(DEV)
     rng = np.random.default_rng(99)

@@ -29,7 +29,8 @@ F32 = 0
 BF16 = 1
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 
-ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_dispatch", "moonep_replicate",
+ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded", "moonep_dispatch",
+                "moonep_replicate",
                 "moonep_combine", "moonep_reduce_dup_grads", "moonep_combine_backward",
                 "moonep_dispatch_backward", "moonep_strerror")
 
@@ -50,7 +51,7 @@ _LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D
                    "Dpre", "dst", "src", "n_dup", "dup_expert", "dup_start", "dup_count",
                    "seg_ptr", "seg_expert", "n_list", "list_expert", "list_rank", "list_b",
                    "dup_ptr", "ws_tile_counts", "ws_tile_status", "ws_mat_pre", "ws_xlist",
-                   "ws_n_x", "ws_piece_js")
+                   "ws_n_x", "ws_piece_js", "ws_kept", "ws_koff", "ws_upre")
 
 
 class Layout(ctypes.Structure):
@@ -63,6 +64,7 @@ _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _P_DIMS, _P_LAY = ctypes.POINTER(Dims), ctypes.POINTER(Layout)
 _lib.moonep_plan_layout.argtypes = [_P_DIMS, _P_LAY]
 _lib.moonep_plan.argtypes = [_P_DIMS, _vp, _vp, _vp]
+_lib.moonep_plan_bounded.argtypes = [_P_DIMS, _vp, _vp, _vp]
 _lib.moonep_dispatch.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp]
 _lib.moonep_replicate.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
 _lib.moonep_combine.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp, _i32, _vp]
@@ -134,6 +136,15 @@ def moonep_plan(dims: Dims, topk_ids, plan_buf, stream=None) -> None:
     ids = _ptr(topk_ids, "topk_ids", torch.int32, 4 * dims.R * dims.S * dims.K)
     pb = _ptr(plan_buf, "plan_buf", None, lay.bytes)
     _check(_lib.moonep_plan(ctypes.byref(dims), ids, pb, _stream(stream, plan_buf)), "moonep_plan")
+
+
+def moonep_plan_bounded(dims: Dims, topk_ids, plan_buf, stream=None) -> None:
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    ids = _ptr(topk_ids, "topk_ids", torch.int32, 4 * dims.R * dims.S * dims.K)
+    pb = _ptr(plan_buf, "plan_buf", None, lay.bytes)
+    _check(_lib.moonep_plan_bounded(ctypes.byref(dims), ids, pb, _stream(stream, plan_buf)),
+           "moonep_plan_bounded")
 
 
 def moonep_dispatch(dims: Dims, plan_buf, hidden, recv, stream=None) -> None:

@@ -87,6 +87,9 @@ PlanPtrs resolve(const moonep_layout &l, void *base) {
     p.xlist = at(l.ws_xlist);
     p.n_x = at(l.ws_n_x);
     p.piece_js = at(l.ws_piece_js);
+    p.kept = at(l.ws_kept);
+    p.koff = at(l.ws_koff);
+    p.upre = at(l.ws_upre);
     return p;
 }
 
@@ -146,20 +149,33 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     l.ws_xlist = take(4 * E);
     l.ws_n_x = take(4);
     l.ws_piece_js = take(4 * (int64_t)l.pcap);
+    l.ws_kept = take(4 * E);
+    l.ws_koff = take(4 * E);
+    l.ws_upre = take(4 * (R + 1));
     l.bytes = off;
     *out = l;
     return MOONEP_OK;
 }
 
-int moonep_plan(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, void *stream) {
+static int plan_common(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, void *stream,
+                       bool bounded) {
     moonep_layout l;
     int rc = moonep_plan_layout(d, &l);
     if (rc != MOONEP_OK) return rc;
     if (!aligned16(topk_ids) || !aligned16(plan_buf)) return MOONEP_ERR_PTR;
     const PlanShape sh = shape_of(d, l);
     (void)hipGetLastError();
-    return launch_rc(launch_plan(sh, topk_ids, resolve(l, plan_buf),
+    return launch_rc(launch_plan(sh, topk_ids, resolve(l, plan_buf), bounded,
                                  static_cast<hipStream_t>(stream)));
+}
+
+int moonep_plan(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, void *stream) {
+    return plan_common(d, topk_ids, plan_buf, stream, false);
+}
+
+int moonep_plan_bounded(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf,
+                        void *stream) {
+    return plan_common(d, topk_ids, plan_buf, stream, true);
 }
 
 int moonep_dispatch(const moonep_dims *d, const void *plan_buf, const void *hidden, void *recv,

@@ -25,6 +25,8 @@ struct PlanPtrs {
     int32_t *n_dup, *dup_expert, *dup_start, *dup_count, *seg_ptr, *seg_expert;
     int32_t *n_list, *list_expert, *list_rank, *list_b, *dup_ptr;
     int32_t *tile_counts, *tile_status, *mat_pre, *xlist, *n_x, *piece_js;
+    int32_t *kept, *koff;  // per expert: rows kept at home, their first row there
+    int32_t *upre;         // [R+1] exclusive prefix over ranks of slots left empty
 };
 
 // Shape constants every kernel needs, computed once on the host.
@@ -40,7 +42,9 @@ struct PlanShape {
 
 PlanPtrs resolve(const moonep_layout &lay, void *base);
 
-hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p,
+// bounded: the plan that keeps at most B duplicates per rank where it can
+// (k_solve_bounded) instead of the water-fill (k_solve).
+hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st);
 
 hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *hidden,

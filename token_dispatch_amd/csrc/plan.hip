@@ -229,65 +229,101 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(PlanShape sh,
     }
 }
 
-// ---------------------------------------------------------------- k_solve
+// ---------------------------------------------------------------- solve
+// The part both solves share: tile status bits and maxT (into *s_status,
+// *s_maxT), T in LDS, the exclusive prefix of T (s_cum), home offsets and home
+// load, keep / overflow / deficit per rank (written to the plan and to s_keep,
+// s_O, s_D). Every thread of the 1024-thread workgroup must call it.
+struct Head {
+    int Te, hoff, keep, O, D;
+};
+
+__device__ Head solve_head(const PlanShape &sh, const PlanPtrs &p, int *s_T, int *s_cum, int *s_keep,
+                           int *s_O, int *s_D, int *s_w, int *s_status, int *s_maxT) {
+    const int tid = threadIdx.x, lane = lane_id();
+    const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
+    Head h{};
+    h.Te = tid < E ? p.T[tid] : 0;
+    int st = 0;
+    for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
+    if (tid == 0) {
+        *s_status = 0;
+        *s_maxT = 0;
+    }
+    if (tid < E) s_T[tid] = h.Te;
+    __syncthreads();
+    if (st) atomicOr(s_status, st);
+    {
+        const int m = wave_max(h.Te);
+        if (lane == 0) atomicMax(s_maxT, m);
+    }
+    // home offsets and load; expert e lives on rank e / G
+    int cum, totT;
+    block_excl_scan<1>(&h.Te, &cum, &totT, s_w);
+    if (tid < E) s_cum[tid] = cum;
+    if (tid == 0) s_cum[E] = totT;
+    __syncthreads();
+    if (tid < E) {
+        h.hoff = cum - s_cum[(tid / G) * G];
+        p.hoff[tid] = h.hoff;
+    }
+    if (tid < R) {
+        const int Lr = s_cum[(tid + 1) * G] - s_cum[tid * G];
+        h.keep = min(Lr, SK);
+        h.O = Lr - h.keep;
+        h.D = SK - h.keep;
+        p.L[tid] = Lr;
+        p.keep[tid] = h.keep;
+        p.O[tid] = h.O;
+        p.D[tid] = h.D;
+        s_keep[tid] = h.keep;
+        s_O[tid] = h.O;
+        s_D[tid] = h.D;
+    }
+    __syncthreads();
+    return h;
+}
+
+// The plan's scalar results, written once every atomic on them has landed.
+__device__ void solve_tail(const PlanShape &sh, const PlanPtrs &p, int n_x, const int *s_status,
+                           const int *s_maxT) {
+    if (threadIdx.x == 0) {
+        const int maxT = *s_maxT;
+        p.n_x[0] = n_x;
+        p.maxT[0] = maxT;
+        p.maxvio[0] = (double)((int64_t)maxT * sh.E) / (double)sh.n_ent - 1.0;
+        p.status[0] = *s_status;
+    }
+}
+
+// ---------------------------------------------------------------- k_solve (water-fill)
 __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
+    __shared__ int s_T[kMaxE];
     __shared__ int s_cum[kMaxE + 1];    // exclusive prefix of T over all experts
     __shared__ int s_ovpre[kMaxE + 1];  // exclusive prefix of each expert's overflow
     __shared__ int s_nzpre[kMaxE + 1];  // exclusive prefix of (overflow > 0)
     __shared__ int s_ovlist[kMaxE];     // experts with overflow, ascending
     __shared__ int s_listE[kMaxE + kMaxR];
-    __shared__ int s_keep[kMaxR], s_Dpre[kMaxR + 1], s_dbeg[kMaxR], s_dend[kMaxR];
-    __shared__ int s_nzlo[kMaxR], s_ppre[kMaxR + 1];
+    __shared__ int s_keep[kMaxR], s_O[kMaxR], s_D[kMaxR], s_Dpre[kMaxR + 1];
+    __shared__ int s_dbeg[kMaxR], s_dend[kMaxR], s_nzlo[kMaxR], s_ppre[kMaxR + 1];
     __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
     __shared__ int s_status, s_maxT;
 
-    const int tid = threadIdx.x, lane = lane_id();
+    const int tid = threadIdx.x;
     const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
-    const int Te = tid < E ? p.T[tid] : 0;
-    int st = 0;
-    for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
-    if (tid == 0) {
-        s_status = 0;
-        s_maxT = 0;
-    }
-    __syncthreads();
-    // 1. tile status bits and maxT (read at the end, after several barriers)
-    if (st) atomicOr(&s_status, st);
-    {
-        const int m = wave_max(Te);
-        if (lane == 0) atomicMax(&s_maxT, m);
-    }
-
-    // 2. home offsets and load. Expert e lives on rank e / G.
-    int cum, totT;
-    block_excl_scan<1>(&Te, &cum, &totT, s_w);
-    if (tid < E) s_cum[tid] = cum;
-    if (tid == 0) s_cum[E] = totT;
-    __syncthreads();
-    int hoff = 0;
-    if (tid < E) {
-        hoff = cum - s_cum[(tid / G) * G];
-        p.hoff[tid] = hoff;
-    }
-    int keep = 0, O = 0, D = 0;
-    if (tid < R) {
-        const int Lr = s_cum[(tid + 1) * G] - s_cum[tid * G];
-        keep = min(Lr, SK);
-        O = Lr - keep;
-        D = SK - keep;
-        p.L[tid] = Lr;
-        p.keep[tid] = keep;
-        p.O[tid] = O;
-        p.D[tid] = D;
-        s_keep[tid] = keep;
-    }
+    const Head h = solve_head(sh, p, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
     // each expert's overflow: the part of its home list [hoff, hoff + T) at or
     // beyond S*K; in the global overflow order (home rank, expert, token, k) --
-    // with contiguous homes simply expert order -- it is [ovpre, ovpre + ov)
-    const int ov = tid < E ? max(hoff + Te, SK) - max(hoff, SK) : 0;
+    // with contiguous homes simply expert order -- it is [ovpre, ovpre + ov).
+    // Its first kept = T - ov entries stay home, from row min(hoff, S*K).
+    const int ov = tid < E ? max(h.hoff + h.Te, SK) - max(h.hoff, SK) : 0;
+    if (tid < E) {
+        p.kept[tid] = h.Te - ov;
+        p.koff[tid] = min(h.hoff, SK);
+    }
 
-    // 3. the water-fill prefix sums of O and D, and of ov and (ov > 0), in one pass
-    int v4[4] = {O, D, ov, ov > 0 ? 1 : 0}, pre[4], tot[4];
+    // the water-fill prefix sums of O and D, and of ov and (ov > 0), in one pass
+    int v4[4] = {h.O, h.D, ov, ov > 0 ? 1 : 0}, pre[4], tot[4];
     block_excl_scan<4>(v4, pre, tot, s_w);
     const int totO = tot[0], totD = tot[1], totNZ = tot[3];
     if (tid < R) {
@@ -309,8 +345,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
     }
     __syncthreads();
 
-    // 4. pieces per deficit rank: overflowing experts whose interval meets the
-    //    rank's filled deficit interval [dbeg, dend).
+    // pieces per deficit rank: overflowing experts whose interval meets the
+    // rank's filled deficit interval [dbeg, dend)
     int np = 0;
     if (tid < R) {
         const int dbeg = min(s_Dpre[tid], totO), dend = min(s_Dpre[tid + 1], totO);
@@ -325,22 +361,26 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         p.n_dup[tid] = np;
         if (np > sh.B) atomicOr(&s_status, MOONEP_STATUS_OVER_B);
     }
-    int v2[2] = {np, tid < R ? min(np, sh.B) : 0}, ppre[2], ptot[2];
-    block_excl_scan<2>(v2, ppre, ptot, s_w);
+    // pieces, materialised duplicates and empty slots (only with dropped ids) per rank
+    int v3[3] = {np, tid < R ? min(np, sh.B) : 0, tid < R ? h.D - (s_dend[tid] - s_dbeg[tid]) : 0};
+    int ppre[3], ptot[3];
+    block_excl_scan<3>(v3, ppre, ptot, s_w);
     const int P = ptot[0];
     if (tid < R) {
         s_ppre[tid] = ppre[0];
         p.mat_pre[tid] = ppre[1];
+        p.upre[tid] = ppre[2];
     }
     if (tid == 0) {
         s_ppre[R] = P;
         p.mat_pre[R] = ptot[1];
+        p.upre[R] = ptot[2];
         p.n_list[0] = P;
     }
     __syncthreads();
 
-    // 5. one thread per piece: rank-major order equals (expert, rank) order
-    //    because both interval families are increasing.
+    // one thread per piece: rank-major order equals (expert, rank) order
+    // because both interval families are increasing
     const int sp = G + sh.dcap + 1, se = G + sh.dcap;
     for (int q = tid; q < P; q += kSolveThreads) {
         const int r = upper_bound(s_ppre, R + 1, q) - 1;
@@ -356,41 +396,298 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         p.list_expert[q] = e;
         p.list_rank[q] = r;
         p.list_b[q] = b;
-        p.piece_js[q] = js;
+        p.piece_js[q] = js - s_ovpre[e];  // first overflow index of the piece within its expert
         p.seg_ptr[(int64_t)r * sp + G + b] = start;
         p.seg_expert[(int64_t)r * se + G + b] = e;
         s_listE[q] = e;
     }
     __syncthreads();
 
-    // 6. CSR of the list over experts; experts with duplicates = overflowing experts
+    // CSR of the list over experts; experts with duplicates = overflowing experts
     for (int e = tid; e <= E; e += kSolveThreads) p.dup_ptr[e] = lower_bound(s_listE, P, e);
     for (int i = tid; i < totNZ; i += kSolveThreads) p.xlist[i] = s_ovlist[i];
 
-    // 7. home segments and the end of each rank's filled rows
+    // home segments and the end of each rank's filled rows
     if (tid < E) {
         const int r = tid / G, i = tid - r * G;
-        p.seg_ptr[(int64_t)r * sp + i] = min(hoff, SK);
+        p.seg_ptr[(int64_t)r * sp + i] = min(h.hoff, SK);
         p.seg_expert[(int64_t)r * se + i] = tid;
     }
-    if (tid < R) p.seg_ptr[(int64_t)tid * sp + G + np] = keep + (s_dend[tid] - s_dbeg[tid]);
+    if (tid < R) p.seg_ptr[(int64_t)tid * sp + G + np] = h.keep + (s_dend[tid] - s_dbeg[tid]);
+    solve_tail(sh, p, totNZ, &s_status, &s_maxT);
+}
 
-    if (tid == 0) {
-        const int maxT = s_maxT;
-        p.n_x[0] = totNZ;
-        p.maxT[0] = maxT;
-        p.maxvio[0] = (double)((int64_t)maxT * E) / (double)sh.n_ent - 1.0;
-        p.status[0] = s_status;
+// ---------------------------------------------------------------- k_solve_bounded
+// The plan that keeps at most B duplicates per rank where it can: an overloaded
+// rank overflows its largest experts first (T descending, then id); deficit ranks
+// are filled one at a time, largest deficit first (then rank id); a rank's
+// pieces 1 .. B-1 are the largest remaining overflow that fits whole (then lowest
+// id), or if none fits a piece of the largest one; its B-th piece is a piece of
+// the smallest remaining overflow that fills the room (then lowest id), or if none
+// is that large the largest one whole, after which the rank goes on the same way
+// over its budget (MOONEP_STATUS_OVER_B). Exact S*K rows per rank and the minimum
+// number of moved rows hold as for the water-fill.
+//
+// The overflows wait in one list sorted by (rows left descending, id), so every
+// choice above is a search for a boundary in it: the first entry that fits, the
+// last entry at least as large as the room and the first entry of that size.
+// Wave 0 runs the placement over that list in LDS, 64 entries per ballot.
+constexpr int kMaxPieces = kMaxE + kMaxR;
+
+// First index i in [0, n) of the list whose left value satisfies pred (n if
+// none); pred must be false on a prefix of the list and true after it.
+template <typename F>
+__device__ __forceinline__ int wave_first(const int *left, int n, F pred) {
+    const int lane = lane_id();
+    for (int c = 0; c < n; c += 64) {
+        const int i = c + lane;
+        const uint64_t m = __ballot(i < n && pred(left[i]));
+        if (m) return c + __ffsll((unsigned long long)m) - 1;
     }
+    return n;
+}
+
+// Orders one wave's LDS writes before its later reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Move list entries (from, to] one place down (entry i+1 to i), ascending, so a
+// lane always reads an entry before the lane below writes over it.
+__device__ __forceinline__ void wave_shift_down(int *a, int *b, int from, int to) {
+    const int lane = lane_id();
+    for (int c = from; c < to; c += 64) {
+        const int i = c + lane;
+        int va = 0, vb = 0;
+        if (i < to) {
+            va = a[i + 1];
+            vb = b[i + 1];
+        }
+        if (i < to) {
+            a[i] = va;
+            b[i] = vb;
+        }
+        wave_lds_sync();
+    }
+}
+
+__global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
+    __shared__ int s_T[kMaxE];
+    __shared__ int s_cum[kMaxE + 1];
+    __shared__ int s_kc[kMaxE + 1];           // exclusive prefix of kept rows
+    __shared__ int s_ov[kMaxE];               // overflow rows of each expert
+    __shared__ int s_left[kMaxE], s_le[kMaxE];  // the sorted list: rows left, expert
+    __shared__ int s_xl[kMaxE];               // overflowing experts in id order
+    __shared__ int s_bin[kMaxR];              // deficit ranks in fill order
+    __shared__ int s_keep[kMaxR], s_O[kMaxR], s_D[kMaxR];
+    __shared__ int s_nd[kMaxR], s_first[kMaxR], s_fill[kMaxR];
+    __shared__ int s_pe[kMaxPieces], s_pr[kMaxPieces], s_pstart[kMaxPieces], s_pcnt[kMaxPieces];
+    __shared__ int s_pjj[kMaxPieces], s_pkey[kMaxPieces];
+    __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
+    __shared__ int s_status, s_maxT, s_np, s_err;
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const int E = sh.E, R = sh.R, G = sh.G, B = sh.B;
+    const Head h = solve_head(sh, p, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
+
+    // 1. overflow of each overloaded rank, from its largest experts
+    int ov = 0;
+    if (tid < E) {
+        const int r = tid / G;
+        int before = 0;  // rows of the rank's experts that come before this one
+        for (int e2 = r * G; e2 < (r + 1) * G; ++e2) {
+            const int t2 = s_T[e2];
+            if (t2 > h.Te || (t2 == h.Te && e2 < tid)) before += t2;
+        }
+        ov = min(max(s_O[r] - before, 0), h.Te);
+        s_ov[tid] = ov;
+    }
+    const int kept = tid < E ? h.Te - ov : 0;
+    int kv[3] = {kept, ov > 0 ? 1 : 0, tid < R && h.D > 0 ? 1 : 0}, kpre[3], ktot[3];
+    block_excl_scan<3>(kv, kpre, ktot, s_w);
+    const int n_items = ktot[1], n_bins = ktot[2];
+    if (tid < E) {
+        s_kc[tid] = kpre[0];
+        if (ov > 0) s_xl[kpre[1]] = tid;
+    }
+    if (tid == 0) {
+        s_kc[E] = ktot[0];
+        s_np = 0;
+        s_err = 0;
+    }
+    int v2[2] = {h.O, h.D}, dpre[2], dtot[2];
+    block_excl_scan<2>(v2, dpre, dtot, s_w);  // also orders the writes above
+    if (tid < R) {
+        p.Opre[tid] = dpre[0];
+        p.Dpre[tid] = dpre[1];
+        s_nd[tid] = 0;
+        s_fill[tid] = 0;
+        s_first[tid] = 0;
+    }
+    if (tid == 0) {
+        p.Opre[R] = dtot[0];
+        p.Dpre[R] = dtot[1];
+    }
+    if (tid < E) {
+        p.kept[tid] = kept;
+        p.koff[tid] = kpre[0] - s_kc[(tid / G) * G];
+    }
+    // the sorted list of overflows: (rows descending, id) -- rank by counting --
+    // and the deficit ranks in fill order (deficit descending, then id)
+    if (tid < n_items) {
+        const int e = s_xl[tid], v = s_ov[e];
+        int pos = 0;
+        for (int i = 0; i < n_items; ++i) {
+            const int e2 = s_xl[i], v2x = s_ov[e2];
+            pos += (v2x > v || (v2x == v && e2 < e)) ? 1 : 0;
+        }
+        s_left[pos] = v;
+        s_le[pos] = e;
+    }
+    if (tid < R && h.D > 0) {
+        int pos = 0;
+        for (int r2 = 0; r2 < R; ++r2) {
+            const int d2 = s_D[r2];
+            pos += (d2 > 0 && (d2 > h.D || (d2 == h.D && r2 < tid))) ? 1 : 0;
+        }
+        s_bin[pos] = tid;
+    }
+    __syncthreads();
+
+    // 2. placement (wave 0): ranks in fill order, pieces by the rules above
+    if (w == 0) {
+        int n = n_items, np = 0;
+        for (int bi = 0; bi < n_bins && n > 0; ++bi) {
+            const int r = s_bin[bi];
+            int room = s_D[r], used = 0;
+            if (lane == 0) s_first[r] = np;
+            while (room > 0 && n > 0) {
+                int idx;
+                if (used < B - 1) {
+                    idx = wave_first(s_left, n, [room](int v) { return v <= room; });
+                    if (idx == n) idx = 0;  // nothing fits: a piece of the largest
+                } else {
+                    const int j = wave_first(s_left, n, [room](int v) { return v < room; }) - 1;
+                    if (j < 0) {
+                        idx = 0;  // nothing fills the room: the largest whole
+                    } else {
+                        const int vj = s_left[j];
+                        idx = wave_first(s_left, n, [vj](int v) { return v <= vj; });
+                    }
+                }
+                const int e = s_le[idx], v = s_left[idx];
+                const int t = min(v, room);
+                if (np >= kMaxPieces || np >= sh.pcap) {
+                    if (lane == 0) s_err = 1;
+                    break;
+                }
+                wave_lds_sync();  // every lane has read s_le / s_left at idx
+                if (lane == 0) {
+                    s_pe[np] = e;
+                    s_pr[np] = r;
+                    s_pstart[np] = s_keep[r] + (s_D[r] - room);
+                    s_pcnt[np] = t;
+                    s_pjj[np] = s_ov[e] - v;
+                }
+                ++np;
+                room -= t;
+                ++used;
+                const int nv = v - t;
+                if (nv == 0) {
+                    // gone: close the gap
+                    wave_shift_down(s_left, s_le, idx, n - 1);
+                    --n;
+                } else {
+                    // smaller now: it moves behind every entry that sorts before it
+                    const int q = wave_first(s_left, n, [nv](int x) { return x < nv; });
+                    int dest = q - 1;  // last entry > nv, or equal with a lower id
+                    // entries equal to nv with a lower id stay before it
+                    while (dest > idx && s_left[dest] == nv && s_le[dest] > e) --dest;
+                    wave_shift_down(s_left, s_le, idx, dest);
+                    if (lane == 0) {
+                        s_left[dest] = nv;
+                        s_le[dest] = e;
+                    }
+                    wave_lds_sync();
+                }
+            }
+            if (lane == 0) {
+                s_nd[r] = used;
+                s_fill[r] = s_D[r] - room;
+            }
+        }
+        if (lane == 0) s_np = np;
+    }
+    __syncthreads();
+
+    // 3. tables: per rank (pieces in placement order), the list by (expert, rank)
+    const int P = s_np;
+    const int sp = G + sh.dcap + 1, se = G + sh.dcap;
+    for (int q = tid; q < P; q += kSolveThreads) {
+        const int r = s_pr[q], e = s_pe[q], b = q - s_first[r];
+        if (b >= sh.dcap) continue;  // cannot happen: a rank takes each expert at most once
+        const int64_t rb = (int64_t)r * sh.dcap + b;
+        p.dup_expert[rb] = e;
+        p.dup_start[rb] = s_pstart[q];
+        p.dup_count[rb] = s_pcnt[q];
+        p.seg_ptr[(int64_t)r * sp + G + b] = s_pstart[q];
+        p.seg_expert[(int64_t)r * se + G + b] = e;
+        s_pkey[q] = e * R + r;  // one piece per (expert, rank)
+    }
+    int nd = 0;
+    if (tid < R) {
+        nd = s_nd[tid];
+        p.n_dup[tid] = nd;
+        if (nd > B) atomicOr(&s_status, MOONEP_STATUS_OVER_B);
+        if (s_err) atomicOr(&s_status, MOONEP_STATUS_BAD_ID);
+    }
+    int mv[2] = {tid < R ? min(nd, B) : 0, tid < R ? h.D - s_fill[tid] : 0}, mpre[2], mtot[2];
+    block_excl_scan<2>(mv, mpre, mtot, s_w);  // also orders the key writes above
+    if (tid < R) {
+        p.mat_pre[tid] = mpre[0];
+        p.upre[tid] = mpre[1];
+    }
+    if (tid == 0) {
+        p.mat_pre[R] = mtot[0];
+        p.upre[R] = mtot[1];
+        p.n_list[0] = P;
+    }
+    for (int q = tid; q < P; q += kSolveThreads) {
+        const int key = s_pkey[q];
+        int pos = 0;
+        for (int i = 0; i < P; ++i) pos += s_pkey[i] < key ? 1 : 0;
+        p.list_expert[pos] = s_pe[q];
+        p.list_rank[pos] = s_pr[q];
+        p.list_b[pos] = q - s_first[s_pr[q]];
+        p.piece_js[pos] = s_pjj[q];
+    }
+    // CSR over experts: pieces of expert e are the keys in [e*R, (e+1)*R)
+    for (int e = tid; e <= E; e += kSolveThreads) {
+        int c = 0;
+        for (int i = 0; i < P; ++i) c += s_pkey[i] < e * R ? 1 : 0;
+        p.dup_ptr[e] = c;
+    }
+    for (int i = tid; i < n_items; i += kSolveThreads) p.xlist[i] = s_xl[i];
+    if (tid < E) {
+        const int r = tid / G, i = tid - r * G;
+        p.seg_ptr[(int64_t)r * sp + i] = kpre[0] - s_kc[r * G];
+        p.seg_expert[(int64_t)r * se + i] = tid;
+    }
+    if (tid < R && nd <= sh.dcap) p.seg_ptr[(int64_t)tid * sp + G + nd] = h.keep + s_fill[tid];
+    solve_tail(sh, p, n_items, &s_status, &s_maxT);
 }
 
 // ---------------------------------------------------------------- k_assign
 // Wave w of the tile takes entries [w*256, w*256 + 256) as kChunks chunks of 64,
-// lane l holding entry w*256 + c*64 + l of chunk c.
+// lane l holding entry w*256 + c*64 + l of chunk c. Both plans place entries the
+// same way: an entry's position among its expert's entries (token, then k order)
+// below kept[e] is a home row from koff[e] on; position kept[e] + jj is overflow
+// row jj of the expert, in the one piece whose range [jj0, jj0 + count) holds it.
 // LDS of k_assign, sized to the problem (ints): see the carve-up below.
 inline size_t assign_lds_bytes(const PlanShape &sh) {
     return sizeof(int32_t) * ((size_t)(kAssignWaves / 2) * sh.E + 3 * (size_t)sh.E + 1 +
-                              2 * (size_t)sh.pcap + 3 * (size_t)sh.R + 2);
+                              3 * (size_t)sh.pcap + (size_t)sh.R + 1);
 }
 
 // Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
@@ -406,14 +703,14 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     // waves 2m (low 16 bits) and 2m+1 (high 16 bits) of every expert: s_pos[m*E + e].
     // A tile has at most 4096 entries, so a half never carries into the other.
     uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
-    int32_t *s_tbase = smem + (kAssignWaves / 2) * E;  // earlier tiles + home offset
-    int32_t *s_home = s_tbase + E;                      // home rank of each expert
-    int32_t *s_dup_ptr = s_home + E;                    // pieces of e: [s_dup_ptr[e], [e+1])
-    int32_t *s_pjs = s_dup_ptr + E + 1;                 // first overflow index of each piece
-    int32_t *s_pslot = s_pjs + sh.pcap;                 // first global slot of each piece
-    int32_t *s_Opre = s_pslot + sh.pcap;                // R + 1
-    int32_t *s_Dpre = s_Opre + R + 1;                   // R + 1
-    int32_t *s_keep = s_Dpre + R + 1;                   // R
+    int32_t *s_tbase = smem + (kAssignWaves / 2) * E;  // entries of e in earlier tiles
+    int32_t *s_kept = s_tbase + E;                      // entries of e kept at home
+    int32_t *s_kslot = s_kept + E;                      // first home slot of e
+    int32_t *s_dup_ptr = s_kslot + E;                   // pieces of e: [s_dup_ptr[e], [e+1])
+    int32_t *s_pjj = s_dup_ptr + E + 1;                 // first overflow row of each piece
+    int32_t *s_pcnt = s_pjj + sh.pcap;                  // rows of each piece
+    int32_t *s_pslot = s_pcnt + sh.pcap;                // first slot of each piece
+    int32_t *s_upre = s_pslot + sh.pcap;                // R + 1
     const int tok0 = tile * sh.tile_tokens;
     const int n = min(sh.tile_tokens, sh.n_tok - tok0) * sh.K;
     const int64_t a0 = (int64_t)tok0 * sh.K;
@@ -428,24 +725,21 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     }
     int gbase = 0;
     if (tid < E) {
-        gbase = p.tile_counts[(int64_t)tile * E + tid] + p.hoff[tid];
-        s_home[tid] = tid / sh.G;
+        gbase = p.tile_counts[(int64_t)tile * E + tid];
+        s_kept[tid] = p.kept[tid];
+        s_kslot[tid] = (tid / sh.G) * SK + p.koff[tid];
+        s_dup_ptr[tid] = p.dup_ptr[tid];
     }
-    if (tid < E) s_dup_ptr[tid] = p.dup_ptr[tid];
-    if (tid < R) {
-        s_Opre[tid] = p.Opre[tid];
-        s_Dpre[tid] = p.Dpre[tid];
-        s_keep[tid] = p.keep[tid];
-    }
+    if (tid < R) s_upre[tid] = p.upre[tid];
     if (tid == 0) {
         s_dup_ptr[E] = p.dup_ptr[E];
-        s_Opre[R] = p.Opre[R];
-        s_Dpre[R] = p.Dpre[R];
+        s_upre[R] = p.upre[R];
     }
     for (int q = tid; q < P; q += kAssignThreads) {
-        const int r = p.list_rank[q];
-        s_pjs[q] = p.piece_js[q];
-        s_pslot[q] = r * SK + p.dup_start[(int64_t)r * sh.dcap + p.list_b[q]];
+        const int64_t rb = (int64_t)p.list_rank[q] * sh.dcap + p.list_b[q];
+        s_pjj[q] = p.piece_js[q];
+        s_pcnt[q] = p.dup_count[rb];
+        s_pslot[q] = p.list_rank[q] * SK + p.dup_start[rb];
     }
 #pragma unroll
     for (int m = 0; m < kAssignWaves / 2; ++m)
@@ -475,7 +769,6 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     }
     __syncthreads();
     // running positions: earlier waves of this tile, relative to the tile base
-    // (earlier tiles + home offset)
     if (tid < E) {
         uint32_t run = 0;
 #pragma unroll
@@ -501,24 +794,24 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
             const int below = __builtin_amdgcn_mbcnt_hi(
                 (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
             const int rel = (int)((s_pos[(w >> 1) * E + e] >> half) & 0xffffu);
-            const int h = s_tbase[e] + rel + below;
+            const int pos = s_tbase[e] + rel + below;
             // the wave's read above is issued before this add (LDS keeps a wave's
             // operations in order); the other wave of the word only adds to its half
             if (lane == 63 - __clzll((long long)mask))
                 atomicAdd(&s_pos[(w >> 1) * E + e], (uint32_t)__popcll(mask) << half);
-            const int r = s_home[e];
+            const int kept = s_kept[e];
             int slot = -1;
-            if (h < SK) {
-                slot = r * SK + h;
+            if (pos < kept) {
+                slot = s_kslot[e] + pos;
             } else {
-                // overflow index j lies in exactly one piece of expert e; the pieces
-                // of an expert are in increasing j
-                const int j = s_Opre[r] + (h - SK);
-                int q = s_dup_ptr[e];
+                const int jj = pos - kept;
                 const int q1 = s_dup_ptr[e + 1];
-                if (q < q1) {
-                    while (q + 1 < q1 && j >= s_pjs[q + 1]) ++q;
-                    slot = s_pslot[q] + (j - s_pjs[q]);
+                for (int q = s_dup_ptr[e]; q < q1; ++q) {
+                    const int d = jj - s_pjj[q];
+                    if ((unsigned)d < (unsigned)s_pcnt[q]) {
+                        slot = s_pslot[q] + d;
+                        break;
+                    }
                 }
             }
             // A correct plan always lands inside the buffer; the guard only keeps a
@@ -555,17 +848,19 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
         p.list_b[x] = -1;
         p.piece_js[x] = -1;
     }
-    // slots that receive nothing (only when some ids were dropped)
-    const int totO = s_Opre[R], totD = s_Dpre[R];
-    for (int j = totO + gt; j < totD; j += gn) {
-        const int r2 = upper_bound(s_Dpre, R + 1, j) - 1;
-        p.src[(int64_t)r2 * SK + s_keep[r2] + (j - s_Dpre[r2])] = -1;
+    // slots that receive nothing (only when some ids were dropped): the last
+    // upre[r+1] - upre[r] slots of rank r
+    const int n_empty = s_upre[R];
+    for (int j = gt; j < n_empty; j += gn) {
+        const int r2 = upper_bound(s_upre, R + 1, j) - 1;
+        const int u = s_upre[r2 + 1] - s_upre[r2];
+        p.src[(int64_t)r2 * SK + (SK - u) + (j - s_upre[r2])] = -1;
     }
 }
 
 }  // namespace
 
-hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p,
+hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st) {
     const dim3 tiles(sh.n_tiles);
 #define MOONEP_COUNT(KM)                                                                    \
@@ -581,7 +876,8 @@ hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &
 #undef MOONEP_COUNT
     hipLaunchKernelGGL(k_scan, dim3((sh.E + 63) / 64), dim3(kScanThreads), 0, st, sh,
                        p.tile_counts, p.T);
-    hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
+    if (bounded) hipLaunchKernelGGL(k_solve_bounded, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
+    else hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
     const size_t lds = assign_lds_bytes(sh);
     if (lds > 65536) {  // beyond the default dynamic LDS limit of a launch
         const hipError_t e = hipFuncSetAttribute((const void *)k_assign,
