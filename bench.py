@@ -26,14 +26,19 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine GB/s (% of HBM peak) + plan latency µs, K3 shape, 1 GPU"
-KERNEL_SOURCES = ("token_dispatch_amd/csrc/move.hip", "token_dispatch_amd/csrc/plan.hip",
-                  "token_dispatch_amd/csrc/api.hip", "token_dispatch_amd/csrc/internal.h",
-                  "token_dispatch_amd/csrc/backward.hip", "token_dispatch_amd/csrc/rows.h")
+_CSRC = "token_dispatch_amd/csrc/"
+KERNEL_SOURCES = tuple(_CSRC + f for f in ("move.hip", "plan.hip", "api.hip", "internal.h",
+                                           "backward.hip", "rows.h"))
+# The sources that define each call's kernels and their launches: a counter
+# summary stays valid for a call while these are unchanged.
+_MOVE_SOURCES = tuple(_CSRC + f for f in ("move.hip", "rows.h", "internal.h"))
+OP_SOURCES = {"dispatch": _MOVE_SOURCES, "combine": _MOVE_SOURCES, "replicate": _MOVE_SOURCES,
+              "reduce": _MOVE_SOURCES, "plan": (_CSRC + "plan.hip", _CSRC + "internal.h")}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -56,24 +61,25 @@ def algorithmic_bytes(wl, n_mat, n_xm):
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
 
 # Library kernels behind each C-ABI call (one call may enqueue several launches).
-OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_assign"), "replicate": ("k_replicate",),
+OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign"),
+              "replicate": ("k_replicate",),
               "dispatch": ("k_dispatch",), "combine": ("k_combine",), "reduce": ("k_reduce",)}
 # (k_combine also serves the backward of dispatch, so traffic is only summed for
 # runs without --with-backward)
 COPY_CAL_BYTES = 1 << 30
 
 
-def traffic_for(op: str, src_hash: str):
+def traffic_for(op: str):
     """HBM bytes per call of `op` from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current sources of that call's kernels; else None."""
     if not os.path.exists(TRAFFIC_PATH):
         return None
     with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != src_hash:
-        return None
     k = rec.get("ops", {}).get(op)
-    return None if k is None else k.get("hbm_bytes_per_call")
+    if k is None or k.get("source_hash") != kernel_source_hash(OP_SOURCES[op]):
+        return None
+    return k.get("hbm_bytes_per_call")
 
 
 def _pmc_rows(csv_path: str, counter: str):
@@ -114,9 +120,43 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, co
             tot = sum(v for _, n, v in rows if any(k + "(" in n or k + "<" in n for k in kernels))
             ent = rec["ops"].setdefault(op, {})
             ent[counter.lower() + "_bytes_per_call"] = tot * 1024.0 * factor / calls
-    for ent in rec["ops"].values():
+    for op, ent in rec["ops"].items():
         ent["hbm_bytes_per_call"] = ent["fetch_size_bytes_per_call"] + ent["write_size_bytes_per_call"]
+        ent["source_hash"] = kernel_source_hash(OP_SOURCES[op])
     return rec
+
+
+def plan_latency(plan_fn, dims, ids_d, plan_buf, stream, iters):
+    """The plan call alone, timed with events on its stream: warm (the ids were
+    just written by a device copy, as a router would leave them) and cold (after
+    1 GiB has streamed through the caches). Median and min in microseconds."""
+    import numpy as np
+    import torch
+    src = ids_d.clone()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=ids_d.device)
+    out = {}
+    for kind in ("warm", "cold"):
+        ts = []
+        for i in range(iters):
+            # the GPU is kept busy ahead of the timed region (a spin, or the flush)
+            # so that the host's launches are queued before the first event runs
+            if kind == "warm":
+                torch.cuda._sleep(200_000)
+                ids_d.copy_(src)
+            else:
+                flush.fill_(float(i))
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            plan_fn(dims, ids_d, plan_buf)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        out[kind + "_median"] = round(float(np.median(ts)), 2)
+        out[kind + "_min"] = round(float(np.min(ts)), 2)
+    out["iters"] = iters
+    del flush, src
+    return out
 
 
 def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
@@ -181,12 +221,18 @@ def main():
     ap.add_argument("--workload", default="k3",
                     choices=["tiny", "uniform", "zipf", "k3", "decode"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--plan", default="waterfill", choices=["waterfill", "bounded"],
+                    help="the plan each step computes: the water-fill (moonep_plan) or the one "
+                         "bounded by B duplicates per rank (moonep_plan_bounded)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--with-backward", action="store_true",
                     help="also time combine-backward (grad_out = out, y = recv) and "
                          "dispatch-backward (grad_recv = grad_y) in every step")
+    ap.add_argument("--plan-iters", type=int, default=30,
+                    help="plan calls timed alone after the steps, warm and cold each "
+                         "(0: skip; also skipped with --copy-calibration)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after the timed steps, one plain device copy of {COPY_CAL_BYTES} bytes "
                          "(the reference dispatch for scaling HBM byte counters)")
@@ -245,10 +291,12 @@ def main():
     if args.with_backward:
         ops += ["combine_backward", "dispatch_backward"]
 
+    plan_fn = td.moonep_plan_bounded if args.plan == "bounded" else td.moonep_plan
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        td.moonep_plan(dims, ids_d, plan_buf)
+        plan_fn(dims, ids_d, plan_buf)
         if ev:
             ev[1].record(stream)
         td.moonep_replicate(dims, plan_buf, expert_w, dup_w, wl.block_bytes)
@@ -288,6 +336,10 @@ def main():
     op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, op in enumerate(ops)}
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    plan_lat = None
+    if args.plan_iters > 0 and not args.copy_calibration:
+        plan_lat = plan_latency(plan_fn, dims, ids_d, plan_buf, stream, args.plan_iters)
+        print(f"# plan latency: {plan_lat}", file=sys.stderr, flush=True)
     if args.copy_calibration:
         a = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -316,11 +368,12 @@ def main():
 
     dom = max(("dispatch", "combine"), key=lambda o: op_ms[o])
     src_hash = kernel_source_hash()
-    traffic = traffic_for(dom, src_hash)
+    traffic = traffic_for(dom)
     roofline = {"bound": "hbm", "achieved": round(gbs[dom], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs[dom] / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": dom, "algorithmic_bytes_per_launch": nbytes[dom],
+                "kernel": dom, "kernel_source_hash": kernel_source_hash(OP_SOURCES[dom]),
+                "algorithmic_bytes_per_launch": nbytes[dom],
                 "avg_launch_ms": round(op_ms[dom], 4),
                 "launch": f"one moonep_{dom} call: a short sequence of k_{dom} launches "
                           "over token chunks, timed as a whole"}
@@ -338,9 +391,10 @@ def main():
         "config": {"workload": f"{wl.name}: R={wl.R} virtual ranks, E={wl.E}, K={wl.K}, "
                                f"S={wl.S}, H={wl.H}, B={wl.B}, weight block "
                                f"{'x'.join(map(str, wl.block_shape))}",
-                   "routing": wl.routing, "seed": args.seed, "parallelism": "ep (virtual, 1 GPU)"},
+                   "routing": wl.routing, "seed": args.seed, "plan": args.plan,
+                   "parallelism": "ep (virtual, 1 GPU)"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "plan_us": round(op_ms["plan"] * 1e3, 2),
+        "plan_us": round(op_ms["plan"] * 1e3, 2), "plan_latency_us": plan_lat,
         "op_ms": {k: round(x, 4) for k, x in op_ms.items()},
         "op_gbs": {k: round(x, 1) for k, x in gbs.items()},
         "maxvio_before": round(maxvio, 4), "rank_maxvio_after": rank_maxvio_after,

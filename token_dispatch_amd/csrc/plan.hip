@@ -40,6 +40,7 @@ static_assert(kMaxE <= kAssignThreads && kMaxR <= kAssignThreads && kMaxE <= kSo
                   kMaxR <= kSolveThreads,
               "one expert or rank per thread (the E-th / R-th prefix entries come from thread 0)");
 static_assert((1 << kMaxIdBits) >= kMaxE, "ids fit the ballot bit slices");
+static_assert(kMaxE <= 1024 && (kMaxE & (kMaxE - 1)) == 0, "expert ids fit the 10-bit field of a packed placement key");
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
@@ -428,62 +429,147 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
 // over its budget (MOONEP_STATUS_OVER_B). Exact S*K rows per rank and the minimum
 // number of moved rows hold as for the water-fill.
 //
-// The overflows wait in one list sorted by (rows left descending, id), so every
-// choice above is a search for a boundary in it: the first entry that fits, the
-// last entry at least as large as the room and the first entry of that size.
-// Wave 0 runs the placement over that list in LDS, 64 entries per ballot.
+// Every rule picks a number of rows first and then the lowest id among the
+// overflows with that many rows left, so one placement step is a few wave-wide
+// maximum reductions over the overflows, which wave 0 holds in registers
+// (kMaxE / 64 per lane): two when (rows, id) packs into one 31-bit key, three
+// otherwise.
 constexpr int kMaxPieces = kMaxE + kMaxR;
+constexpr int kItemsPerLane = kMaxE / 64;
 
-// First index i in [0, n) of the list whose left value satisfies pred (n if
-// none); pred must be false on a prefix of the list and true after it.
-template <typename F>
-__device__ __forceinline__ int wave_first(const int *left, int n, F pred) {
-    const int lane = lane_id();
-    for (int c = 0; c < n; c += 64) {
-        const int i = c + lane;
-        const uint64_t m = __ballot(i < n && pred(left[i]));
-        if (m) return c + __ffsll((unsigned long long)m) - 1;
-    }
-    return n;
+// Maximum over the 64 lanes, in every lane: DPP shifts inside each 16-lane row,
+// then rows 0 -> 1 and 1 -> 2,3 broadcasts (lane 63 ends with the maximum).
+__device__ __forceinline__ int wave_reduce_max(int x) {
+    constexpr int kLo = -2147483647 - 1;
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(x, 63);
 }
 
-// Orders one wave's LDS writes before its later reads by other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+struct PlaceArgs {
+    int n_items, n_bins, B, cap;
+    const int *s_xl, *s_ov;
+    const int *s_bin, *s_binD, *s_binK;  // deficit ranks in fill order: rank, D, keep
+    int *s_first, *s_nd, *s_fill, *s_pe, *s_pr, *s_pstart, *s_pcnt, *s_pjj;
+};
+
+// The placement, run by one wave: ranks in fill order, pieces by the rules
+// above. Lane l holds overflows l, l + 64, ... of the id-ordered list in NS
+// register slots (so within a lane a lower slot is a lower id); the lane that
+// holds the chosen overflow records the piece. Returns the number of pieces, or
+// -(pieces + 1) if the piece tables ran out of room (cannot happen: pieces <=
+// overflowing experts + deficit ranks - 1).
+template <int NS, bool PACKED>
+__device__ __forceinline__ int place_pieces(const PlaceArgs &a) {
+    constexpr int kLo = -2147483647 - 1;
+    constexpr int kVmax = (1 << 21) - 1;  // PACKED: rows left fit 21 bits, ids 10
+    const int lane = lane_id();
+    int lv[NS], lid[NS], lov[NS];  // rows left (0: placed), expert id (-1: none), overflow rows
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+        const int i = c * 64 + lane;
+        lid[c] = i < a.n_items ? a.s_xl[i] : -1;
+        lov[c] = lid[c] >= 0 ? a.s_ov[lid[c]] : 0;
+        lv[c] = lov[c];
+    }
+    int n = a.n_items, np = 0;
+    int r_nx = a.s_bin[0], D_nx = a.s_binD[0], K_nx = a.s_binK[0];  // the next rank, loaded ahead
+    for (int bi = 0; bi < a.n_bins && n > 0; ++bi) {
+        const int r = r_nx, D = D_nx, keep = K_nx;
+        if (bi + 1 < a.n_bins) {
+            r_nx = a.s_bin[bi + 1];
+            D_nx = a.s_binD[bi + 1];
+            K_nx = a.s_binK[bi + 1];
+        }
+        int room = D, used = 0;
+        if (lane == 0) a.s_first[r] = np;
+        while (room > 0 && n > 0) {
+            if (np >= a.cap) return -(np + 1);
+            const bool fit_rule = used < a.B - 1;
+            int v, e;
+            if constexpr (PACKED) {
+                // one key per overflow, larger = preferred: (rows, lowest id) for the
+                // whole-fit rule and the largest, (fewest rows, lowest id) for the
+                // filling rule; -1 = not a candidate
+                int pk = -1, fk = -1;
+#pragma unroll
+                for (int c = 0; c < NS; ++c) {
+                    const int x = lv[c], low = (kMaxE - 1) - lid[c];
+                    const int big = (x << 10) | low;
+                    fk = max(fk, x > 0 ? big : -1);
+                    if (fit_rule) pk = max(pk, x > 0 && x <= room ? big : -1);
+                    else pk = max(pk, x >= room ? ((kVmax - x) << 10) | low : -1);
+                }
+                const int pm = wave_reduce_max(pk), fm = wave_reduce_max(fk);
+                const int k = pm >= 0 ? pm : fm;
+                e = (kMaxE - 1) - (k & (kMaxE - 1));
+                v = pm >= 0 && !fit_rule ? kVmax - (k >> 10) : k >> 10;
+            } else {
+                // this lane's candidate numbers of rows: by the rule (as a maximum)
+                // and the largest; then the lowest id with that many rows left
+                int pv = kLo, fv = kLo;
+#pragma unroll
+                for (int c = 0; c < NS; ++c) {
+                    fv = max(fv, lv[c]);
+                    if (fit_rule) pv = max(pv, lv[c] > 0 && lv[c] <= room ? lv[c] : kLo);
+                    else pv = max(pv, lv[c] >= room ? -lv[c] : kLo);
+                }
+                const int pm = wave_reduce_max(pv), fm = wave_reduce_max(fv);
+                v = pm != kLo ? (fit_rule ? pm : -pm) : fm;
+                int key = -1;
+#pragma unroll
+                for (int c = NS - 1; c >= 0; --c) key = lv[c] == v ? 0x7fffffff - lid[c] : key;
+                e = 0x7fffffff - wave_reduce_max(key);
+            }
+            const int t = min(v, room);
+            int jj0 = -1;
+#pragma unroll
+            for (int c = 0; c < NS; ++c) {
+                const bool mine = lid[c] == e;
+                jj0 = mine ? lov[c] - v : jj0;
+                lv[c] = mine ? v - t : lv[c];
+            }
+            if (jj0 >= 0) {
+                a.s_pe[np] = e;
+                a.s_pr[np] = r;
+                a.s_pstart[np] = keep + (D - room);
+                a.s_pcnt[np] = t;
+                a.s_pjj[np] = jj0;
+            }
+            ++np;
+            room -= t;
+            ++used;
+            n -= v == t ? 1 : 0;
+        }
+        if (lane == 0) {
+            a.s_nd[r] = used;
+            a.s_fill[r] = D - room;
+        }
+    }
+    return np;
 }
 
-// Move list entries (from, to] one place down (entry i+1 to i), ascending, so a
-// lane always reads an entry before the lane below writes over it.
-__device__ __forceinline__ void wave_shift_down(int *a, int *b, int from, int to) {
-    const int lane = lane_id();
-    for (int c = from; c < to; c += 64) {
-        const int i = c + lane;
-        int va = 0, vb = 0;
-        if (i < to) {
-            va = a[i + 1];
-            vb = b[i + 1];
-        }
-        if (i < to) {
-            a[i] = va;
-            b[i] = vb;
-        }
-        wave_lds_sync();
-    }
+template <int NS>
+__device__ __forceinline__ int place_pieces(const PlaceArgs &a, bool packed) {
+    return packed ? place_pieces<NS, true>(a) : place_pieces<NS, false>(a);
 }
 
 __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
     __shared__ int s_T[kMaxE];
     __shared__ int s_cum[kMaxE + 1];
-    __shared__ int s_kc[kMaxE + 1];           // exclusive prefix of kept rows
-    __shared__ int s_ov[kMaxE];               // overflow rows of each expert
-    __shared__ int s_left[kMaxE], s_le[kMaxE];  // the sorted list: rows left, expert
-    __shared__ int s_xl[kMaxE];               // overflowing experts in id order
-    __shared__ int s_bin[kMaxR];              // deficit ranks in fill order
+    __shared__ int s_kc[kMaxE + 1];   // exclusive prefix of kept rows
+    __shared__ int s_ov[kMaxE];       // overflow rows of each expert
+    __shared__ int s_xl[kMaxE];       // overflowing experts in id order
+    __shared__ int s_bin[kMaxR + 1], s_binD[kMaxR + 1], s_binK[kMaxR + 1];  // deficit ranks in fill order
+    __shared__ uint64_t s_bkey[kMaxR];  // fill-order key of each rank (0: no deficit)
     __shared__ int s_keep[kMaxR], s_O[kMaxR], s_D[kMaxR];
     __shared__ int s_nd[kMaxR], s_first[kMaxR], s_fill[kMaxR];
     __shared__ int s_pe[kMaxPieces], s_pr[kMaxPieces], s_pstart[kMaxPieces], s_pcnt[kMaxPieces];
-    __shared__ int s_pjj[kMaxPieces], s_pkey[kMaxPieces];
+    __shared__ int s_pjj[kMaxPieces], s_pkey[kMaxPieces], s_skey[kMaxPieces];
     __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
     __shared__ int s_status, s_maxT, s_np, s_err;
 
@@ -498,11 +584,13 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
         int before = 0;  // rows of the rank's experts that come before this one
         for (int e2 = r * G; e2 < (r + 1) * G; ++e2) {
             const int t2 = s_T[e2];
-            if (t2 > h.Te || (t2 == h.Te && e2 < tid)) before += t2;
+            before += (t2 > h.Te || (t2 == h.Te && e2 < tid)) ? t2 : 0;
         }
         ov = min(max(s_O[r] - before, 0), h.Te);
         s_ov[tid] = ov;
     }
+    if (tid < R)  // deficit descending, then rank ascending
+        s_bkey[tid] = h.D > 0 ? ((uint64_t)(uint32_t)h.D << 32) | (uint32_t)(0x7fffffff - tid) : 0;
     const int kept = tid < E ? h.Te - ov : 0;
     int kv[3] = {kept, ov > 0 ? 1 : 0, tid < R && h.D > 0 ? 1 : 0}, kpre[3], ktot[3];
     block_excl_scan<3>(kv, kpre, ktot, s_w);
@@ -515,6 +603,15 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
         s_kc[E] = ktot[0];
         s_np = 0;
         s_err = 0;
+    }
+    if (tid < R && h.D > 0) {  // the rank's place in fill order
+        const uint64_t mine = s_bkey[tid];
+        int pos = 0;
+#pragma unroll 8
+        for (int r2 = 0; r2 < R; ++r2) pos += s_bkey[r2] > mine ? 1 : 0;
+        s_bin[pos] = tid;
+        s_binD[pos] = h.D;
+        s_binK[pos] = h.keep;
     }
     int v2[2] = {h.O, h.D}, dpre[2], dtot[2];
     block_excl_scan<2>(v2, dpre, dtot, s_w);  // also orders the writes above
@@ -533,91 +630,24 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
         p.kept[tid] = kept;
         p.koff[tid] = kpre[0] - s_kc[(tid / G) * G];
     }
-    // the sorted list of overflows: (rows descending, id) -- rank by counting --
-    // and the deficit ranks in fill order (deficit descending, then id)
-    if (tid < n_items) {
-        const int e = s_xl[tid], v = s_ov[e];
-        int pos = 0;
-        for (int i = 0; i < n_items; ++i) {
-            const int e2 = s_xl[i], v2x = s_ov[e2];
-            pos += (v2x > v || (v2x == v && e2 < e)) ? 1 : 0;
-        }
-        s_left[pos] = v;
-        s_le[pos] = e;
-    }
-    if (tid < R && h.D > 0) {
-        int pos = 0;
-        for (int r2 = 0; r2 < R; ++r2) {
-            const int d2 = s_D[r2];
-            pos += (d2 > 0 && (d2 > h.D || (d2 == h.D && r2 < tid))) ? 1 : 0;
-        }
-        s_bin[pos] = tid;
-    }
     __syncthreads();
 
-    // 2. placement (wave 0): ranks in fill order, pieces by the rules above
+    // 2. placement (wave 0), with as many register slots per lane as the overflows need
     if (w == 0) {
-        int n = n_items, np = 0;
-        for (int bi = 0; bi < n_bins && n > 0; ++bi) {
-            const int r = s_bin[bi];
-            int room = s_D[r], used = 0;
-            if (lane == 0) s_first[r] = np;
-            while (room > 0 && n > 0) {
-                int idx;
-                if (used < B - 1) {
-                    idx = wave_first(s_left, n, [room](int v) { return v <= room; });
-                    if (idx == n) idx = 0;  // nothing fits: a piece of the largest
-                } else {
-                    const int j = wave_first(s_left, n, [room](int v) { return v < room; }) - 1;
-                    if (j < 0) {
-                        idx = 0;  // nothing fills the room: the largest whole
-                    } else {
-                        const int vj = s_left[j];
-                        idx = wave_first(s_left, n, [vj](int v) { return v <= vj; });
-                    }
-                }
-                const int e = s_le[idx], v = s_left[idx];
-                const int t = min(v, room);
-                if (np >= kMaxPieces || np >= sh.pcap) {
-                    if (lane == 0) s_err = 1;
-                    break;
-                }
-                wave_lds_sync();  // every lane has read s_le / s_left at idx
-                if (lane == 0) {
-                    s_pe[np] = e;
-                    s_pr[np] = r;
-                    s_pstart[np] = s_keep[r] + (s_D[r] - room);
-                    s_pcnt[np] = t;
-                    s_pjj[np] = s_ov[e] - v;
-                }
-                ++np;
-                room -= t;
-                ++used;
-                const int nv = v - t;
-                if (nv == 0) {
-                    // gone: close the gap
-                    wave_shift_down(s_left, s_le, idx, n - 1);
-                    --n;
-                } else {
-                    // smaller now: it moves behind every entry that sorts before it
-                    const int q = wave_first(s_left, n, [nv](int x) { return x < nv; });
-                    int dest = q - 1;  // last entry > nv, or equal with a lower id
-                    // entries equal to nv with a lower id stay before it
-                    while (dest > idx && s_left[dest] == nv && s_le[dest] > e) --dest;
-                    wave_shift_down(s_left, s_le, idx, dest);
-                    if (lane == 0) {
-                        s_left[dest] = nv;
-                        s_le[dest] = e;
-                    }
-                    wave_lds_sync();
-                }
-            }
-            if (lane == 0) {
-                s_nd[r] = used;
-                s_fill[r] = s_D[r] - room;
-            }
+        PlaceArgs a{n_items, n_bins, B, min(kMaxPieces, sh.pcap), s_xl, s_ov, s_bin, s_binD, s_binK,
+                    s_first, s_nd, s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj};
+        const int nslots = (n_items + 63) >> 6;
+        const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
+        int np;
+        if (nslots <= 1) np = place_pieces<1>(a, packed);
+        else if (nslots <= 2) np = place_pieces<2>(a, packed);
+        else if (nslots <= 4) np = place_pieces<4>(a, packed);
+        else if (nslots <= 8) np = place_pieces<8>(a, packed);
+        else np = place_pieces<kItemsPerLane>(a, packed);
+        if (lane == 0) {
+            s_np = np < 0 ? -np - 1 : np;
+            s_err = np < 0 ? 1 : 0;
         }
-        if (lane == 0) s_np = np;
     }
     __syncthreads();
 
@@ -626,6 +656,7 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
     const int sp = G + sh.dcap + 1, se = G + sh.dcap;
     for (int q = tid; q < P; q += kSolveThreads) {
         const int r = s_pr[q], e = s_pe[q], b = q - s_first[r];
+        s_pkey[q] = e * R + r;  // one piece per (expert, rank)
         if (b >= sh.dcap) continue;  // cannot happen: a rank takes each expert at most once
         const int64_t rb = (int64_t)r * sh.dcap + b;
         p.dup_expert[rb] = e;
@@ -633,7 +664,6 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
         p.dup_count[rb] = s_pcnt[q];
         p.seg_ptr[(int64_t)r * sp + G + b] = s_pstart[q];
         p.seg_expert[(int64_t)r * se + G + b] = e;
-        s_pkey[q] = e * R + r;  // one piece per (expert, rank)
     }
     int nd = 0;
     if (tid < R) {
@@ -656,18 +686,17 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
     for (int q = tid; q < P; q += kSolveThreads) {
         const int key = s_pkey[q];
         int pos = 0;
+#pragma unroll 8
         for (int i = 0; i < P; ++i) pos += s_pkey[i] < key ? 1 : 0;
+        s_skey[pos] = key;
         p.list_expert[pos] = s_pe[q];
         p.list_rank[pos] = s_pr[q];
         p.list_b[pos] = q - s_first[s_pr[q]];
         p.piece_js[pos] = s_pjj[q];
     }
+    __syncthreads();
     // CSR over experts: pieces of expert e are the keys in [e*R, (e+1)*R)
-    for (int e = tid; e <= E; e += kSolveThreads) {
-        int c = 0;
-        for (int i = 0; i < P; ++i) c += s_pkey[i] < e * R ? 1 : 0;
-        p.dup_ptr[e] = c;
-    }
+    for (int e = tid; e <= E; e += kSolveThreads) p.dup_ptr[e] = lower_bound(s_skey, P, e * R);
     for (int i = tid; i < n_items; i += kSolveThreads) p.xlist[i] = s_xl[i];
     if (tid < E) {
         const int r = tid / G, i = tid - r * G;
