@@ -6,7 +6,10 @@ compared bit for bit too, which is stricter than the 1e-5 relative bound the
 path promises (that bound is also asserted on the fp32 combine output).
 
 Both plans are covered: the water-fill (moonep_plan) and the plan bounded by B
-duplicates per rank (moonep_plan_bounded), each against its oracle.
+duplicates per rank (moonep_plan_bounded), each against its oracle; the
+water-fill in both of its forms: one kernel for shapes of at most 64 tiles
+("fused", required where a test names it, so the test fails if that path is
+not taken) and four kernels ("multi").
 
 Small shapes are compared element by element; they span several plan tiles with
 a ragged last tile and rows whose 16-byte chunk count does not fill the lanes.
@@ -21,8 +24,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, read_plan, run_plan,
-                              say)
+from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, plan_launch, read_plan,
+                              run_plan, say)
 from tests.invariants import check_plan
 
 pytestmark = pytest.mark.gpu
@@ -139,11 +142,17 @@ def _full_case(td, wl, ids, w, seed, bounded=False):
     return g
 
 
-@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
+# the water-fill in its one-launch and four-launch forms; the bounded plan has only the latter
+PLANS = pytest.mark.parametrize("bounded,launch", [(False, "fused"), (False, "multi"), (True, None)],
+                                ids=["waterfill-fused", "waterfill-multi", "bounded"])
+
+
+@PLANS
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_small_shapes_elementwise(td, wl, bounded):
+def test_small_shapes_elementwise(td, wl, bounded, launch):
     ids, w = W.make_routing(wl, seed=3)
-    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
+    with plan_launch(launch):
+        _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
 
 
 def test_hand_worked_examples_on_gpu(td):
@@ -198,8 +207,8 @@ def test_bounded_hand_worked_examples_on_gpu(td):
         assert_plan_equal(g, oracle.plan(R, E, K, S, B, ids, bounded=True))
 
 
-@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
-def test_invalid_and_repeated_ids(td, bounded):
+@PLANS
+def test_invalid_and_repeated_ids(td, bounded, launch):
     wl = _wl("bad_ids", 4, 32, 4, 1500, 4, 64, W.BF16, 2.0)
     rng = np.random.default_rng(17)
     ids, w = W.make_routing(wl, seed=5)
@@ -207,29 +216,33 @@ def test_invalid_and_repeated_ids(td, bounded):
     w = w.reshape(-1)
     bad = rng.choice(ids.size, 40, replace=False)
     ids[bad] = rng.choice([-1, -100, wl.E, wl.E + 7], 40)
-    g = _full_case(td, wl, ids, w, 5, bounded)
+    with plan_launch(launch):
+        g = _full_case(td, wl, ids, w, 5, bounded)
     assert int(g["status"][0]) & 1
     ids2, w2 = W.make_routing(wl, seed=6)
     ids2 = ids2.reshape(-1, wl.K).copy()
     t = rng.choice(wl.n_tok, 25, replace=False)
     ids2[t, 2] = ids2[t, 0]
-    g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6, bounded)
+    with plan_launch(launch):
+        g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6, bounded)
     assert int(g["status"][0]) & 2
 
 
-@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
-def test_extreme_skew_and_balance(td, bounded):
+@PLANS
+def test_extreme_skew_and_balance(td, bounded, launch):
     # every token picks the same K experts, all homed on rank 0
     wl = _wl("one_hot_rank", 8, 64, 8, 1000, 8, 64, W.BF16, 0.0)
     ids = np.tile(np.arange(8, dtype=np.int32), wl.n_tok)
     w = np.full(ids.size, 1.0 / 8, np.float32)
-    g = _full_case(td, wl, ids, w, 1, bounded)
+    with plan_launch(launch):
+        g = _full_case(td, wl, ids, w, 1, bounded)
     assert int(g["n_dup"].sum()) > 0 and int(g["L"][0]) == wl.n_ent
     # perfectly balanced routing: no overflow, no duplicates
     wl = _wl("balanced", 4, 16, 4, 256, 2, 64, W.BF16, 0.0)
     ids = (np.arange(wl.n_ent) % wl.E).astype(np.int32)
     w = np.full(ids.size, 0.25, np.float32)
-    g = _full_case(td, wl, ids, w, 2, bounded)
+    with plan_launch(launch):
+        g = _full_case(td, wl, ids, w, 2, bounded)
     assert int(g["n_dup"].sum()) == 0 and float(g["maxvio"][0]) == 0.0
 
 
@@ -249,25 +262,28 @@ def test_identity_expert_mean_returns_hidden(td):
     assert torch.equal(out.view(torch.int16), hid.view(torch.int16))
 
 
-def test_deterministic_and_stream_ordered(td):
-    wl = W.WORKLOADS["zipf"].replace(S=2048)
+@pytest.mark.parametrize("launch", ["fused", "multi"])
+def test_deterministic_and_stream_ordered(td, launch):
+    wl = W.WORKLOADS["zipf"].replace(S=512)
     dims = _dims(td, wl)
     ids, _ = W.make_routing(wl, seed=1)
     s = torch.cuda.Stream(DEV)
     bufs = []
     for _ in range(3):
         pb = td.new_plan_buffer(dims, DEV)
-        with torch.cuda.stream(s):
+        with torch.cuda.stream(s), plan_launch(launch):
             ids_d = torch.from_numpy(ids).to(DEV, non_blocking=False)
             td.moonep_plan(dims, ids_d, pb, stream=s)
         bufs.append(pb)
     torch.cuda.synchronize()
     a = read_plan(td, dims, bufs[0])
+    assert_plan_equal(a, oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids))
     for pb in bufs[1:]:
         assert_plan_equal(read_plan(td, dims, pb), a)
 
 
-def test_plan_buffer_reuse_across_shapes(td):
+@pytest.mark.parametrize("launch", ["fused", "multi"])
+def test_plan_buffer_reuse_across_shapes(td, launch):
     """A plan buffer first used for a larger problem gives the same plan for a
     smaller one (no stale state leaks into the result)."""
     big = _wl("big", 8, 64, 8, 2000, 8, 64, W.BF16, 2.5)
@@ -275,26 +291,80 @@ def test_plan_buffer_reuse_across_shapes(td):
     dims_b, dims_s = _dims(td, big), _dims(td, small)
     pb = td.new_plan_buffer(dims_b, DEV)
     ids_b, _ = W.make_routing(big, seed=4)
-    run_plan(td, dims_b, ids_b, DEV, pb)
     ids_s, _ = W.make_routing(small, seed=4)
     lay = td.moonep_plan_layout(dims_s)
-    run_plan(td, dims_s, ids_s, DEV, pb[:lay.bytes])
+    with plan_launch(launch):
+        run_plan(td, dims_b, ids_b, DEV, pb)
+        run_plan(td, dims_s, ids_s, DEV, pb[:lay.bytes])
     g = read_plan(td, dims_s, pb[:lay.bytes])
     assert_plan_equal(g, oracle.plan(small.R, small.E, small.K, small.S, small.B, ids_s))
 
 
+def test_fused_plan_from_arbitrary_buffer_contents(td):
+    """The one-launch plan's workgroups synchronise through words of the plan
+    buffer; any starting contents must work, and so must the values each call
+    leaves for the next."""
+    wl = _wl("sync", 8, 64, 8, 1500, 8, 64, W.BF16, 2.0)
+    dims = _dims(td, wl)
+    lay = td.moonep_plan_layout(dims)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    for fill in ("as allocated", "ones", "random"):
+        pb = td.new_plan_buffer(dims, DEV)
+        if fill == "ones":
+            pb.fill_(255)
+        elif fill == "random":
+            pb.copy_(torch.randint(0, 256, (lay.bytes,), generator=gen, device=DEV,
+                                   dtype=torch.int32).to(torch.uint8))
+        for seed in (0, 1, 2):
+            ids, _ = W.make_routing(wl, seed)
+            with plan_launch("fused"):
+                run_plan(td, dims, ids, DEV, pb)
+            assert_plan_equal(read_plan(td, dims, pb), oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids))
+
+
+def test_fused_plan_graph_replays(td):
+    """A captured one-launch plan replayed on new ids: every replay reads the
+    generation afresh, so each one waits for its own tiles."""
+    wl = _wl("graph", 8, 64, 8, 1000, 8, 64, W.BF16, 2.0)
+    dims = _dims(td, wl)
+    pb = td.new_plan_buffer(dims, DEV)
+    ids0, _ = W.make_routing(wl, 0)
+    ids_d = torch.from_numpy(ids0).to(DEV)
+    s = torch.cuda.Stream(DEV)
+    with plan_launch("fused"):
+        with torch.cuda.stream(s):
+            td.moonep_plan(dims, ids_d, pb, stream=s)  # sets kernel attributes before capture
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            td.moonep_plan(dims, ids_d, pb, stream=s)
+    for seed in (1, 2, 3, 1):
+        ids, _ = W.make_routing(wl, seed)
+        ids_d.copy_(torch.from_numpy(ids).to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_plan_equal(read_plan(td, dims, pb), oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids))
+
+
 # ------------------------------------------------------------ full-size shapes
 
-@pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
-@pytest.mark.parametrize("name", ["tiny", "uniform", "zipf", "k3", "decode"])
-def test_workload_plans_all_seeds(td, name, bounded):
+# tiny, uniform and decode have at most 64 tiles: the water-fill in both forms
+@pytest.mark.parametrize("name,bounded,launch", [
+    ("tiny", False, "fused"), ("tiny", False, "multi"), ("tiny", True, None),
+    ("uniform", False, "fused"), ("uniform", False, "multi"), ("uniform", True, None),
+    ("zipf", False, None), ("zipf", True, None), ("k3", False, None), ("k3", True, None),
+    ("decode", False, "fused"), ("decode", False, "multi"), ("decode", True, None)])
+def test_workload_plans_all_seeds(td, name, bounded, launch):
     wl = W.WORKLOADS[name]
     dims = _dims(td, wl)
     pb = td.new_plan_buffer(dims, DEV)
     for seed in (0, 1, 2):
-        say(f"plan {name} seed {seed} bounded={bounded}")
+        say(f"plan {name} seed {seed} bounded={bounded} launch={launch}")
         ids, _ = W.make_routing(wl, seed)
-        run_plan(td, dims, ids, DEV, pb, bounded=bounded)
+        with plan_launch(launch):
+            run_plan(td, dims, ids, DEV, pb, bounded=bounded)
         g = read_plan(td, dims, pb)
         p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
         assert_plan_equal(g, p)

@@ -26,6 +26,9 @@
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
 // waves of this tile) + (earlier chunks of this wave) + (earlier lanes of the
 // same 64-entry chunk), each an integer count taken in entry order.
+#include <stdlib.h>
+#include <string.h>
+
 #include "internal.h"
 
 namespace moonep {
@@ -297,18 +300,102 @@ __device__ void solve_tail(const PlanShape &sh, const PlanPtrs &p, int n_x, cons
     }
 }
 
-// ---------------------------------------------------------------- k_solve (water-fill)
-__global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
-    __shared__ int s_T[kMaxE];
-    __shared__ int s_cum[kMaxE + 1];    // exclusive prefix of T over all experts
-    __shared__ int s_ovpre[kMaxE + 1];  // exclusive prefix of each expert's overflow
-    __shared__ int s_nzpre[kMaxE + 1];  // exclusive prefix of (overflow > 0)
-    __shared__ int s_ovlist[kMaxE];     // experts with overflow, ascending
-    __shared__ int s_listE[kMaxE + kMaxR];
-    __shared__ int s_keep[kMaxR], s_O[kMaxR], s_D[kMaxR], s_Dpre[kMaxR + 1];
-    __shared__ int s_dbeg[kMaxR], s_dend[kMaxR], s_nzlo[kMaxR], s_ppre[kMaxR + 1];
-    __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
-    __shared__ int s_status, s_maxT;
+// ---------------------------------------------------------------- LDS of the solves
+// Both solves carve their LDS from one int block sized to the problem (E, R,
+// pcap); the same function gives the host the size and the device the arrays.
+struct LdsCarve {
+    int32_t *base;
+    int off;
+    __host__ __device__ int32_t *take(int n) {
+        int32_t *r = base ? base + off : nullptr;
+        off += n;
+        return r;
+    }
+};
+
+constexpr int kScanScratch = (kSolveThreads / 64 + 1) * 4;  // block_excl_scan<NV <= 4>
+
+struct WfLds {
+    int32_t *T, *cum, *ovpre, *nzpre, *ovlist, *listE;
+    int32_t *keep, *O, *D, *Dpre, *dbeg, *dend, *nzlo, *ppre, *w, *scal;
+};
+
+__host__ __device__ inline int wf_lds(int E, int R, int pcap, int32_t *base, WfLds *o) {
+    LdsCarve c{base, 0};
+    WfLds l;
+    l.T = c.take(E);
+    l.cum = c.take(E + 1);     // exclusive prefix of T over all experts
+    l.ovpre = c.take(E + 1);   // exclusive prefix of each expert's overflow
+    l.nzpre = c.take(E + 1);   // exclusive prefix of (overflow > 0)
+    l.ovlist = c.take(E);      // experts with overflow, ascending
+    l.listE = c.take(pcap);
+    l.keep = c.take(R);
+    l.O = c.take(R);
+    l.D = c.take(R);
+    l.Dpre = c.take(R + 1);
+    l.dbeg = c.take(R);
+    l.dend = c.take(R);
+    l.nzlo = c.take(R);
+    l.ppre = c.take(R + 1);
+    l.w = c.take(kScanScratch);
+    l.scal = c.take(4);        // status, maxT
+    if (o) *o = l;
+    return c.off;
+}
+
+struct BdLds {
+    uint64_t *bkey;
+    int32_t *T, *cum, *kc, *ov, *xl, *bin, *binD, *binK, *keep, *O, *D, *nd, *first, *fill;
+    int32_t *pe, *pr, *pstart, *pcnt, *pjj, *pkey, *skey, *w, *scal;
+};
+
+__host__ __device__ inline int bd_lds(int E, int R, int pcap, int32_t *base, BdLds *o) {
+    LdsCarve c{base, 0};
+    BdLds l;
+    l.bkey = reinterpret_cast<uint64_t *>(c.take(2 * R));  // first: 8-byte aligned
+    l.T = c.take(E);
+    l.cum = c.take(E + 1);
+    l.kc = c.take(E + 1);      // exclusive prefix of kept rows
+    l.ov = c.take(E);          // overflow rows of each expert
+    l.xl = c.take(E);          // overflowing experts in id order
+    l.bin = c.take(R + 1);     // deficit ranks in fill order: rank, D, keep
+    l.binD = c.take(R + 1);
+    l.binK = c.take(R + 1);
+    l.keep = c.take(R);
+    l.O = c.take(R);
+    l.D = c.take(R);
+    l.nd = c.take(R);
+    l.first = c.take(R);
+    l.fill = c.take(R);
+    l.pe = c.take(pcap);
+    l.pr = c.take(pcap);
+    l.pstart = c.take(pcap);
+    l.pcnt = c.take(pcap);
+    l.pjj = c.take(pcap);
+    l.pkey = c.take(pcap);
+    l.skey = c.take(pcap);
+    l.w = c.take(kScanScratch);
+    l.scal = c.take(4);        // status, maxT, pieces, error
+    if (o) *o = l;
+    return c.off;
+}
+
+inline size_t solve_lds_bytes(const PlanShape &sh, bool bounded) {
+    const int n = bounded ? bd_lds(sh.E, sh.R, sh.pcap, nullptr, nullptr)
+                          : wf_lds(sh.E, sh.R, sh.pcap, nullptr, nullptr);
+    return sizeof(int32_t) * (size_t)n;
+}
+
+// ---------------------------------------------------------------- water-fill solve
+// One 1024-thread workgroup; smem holds wf_lds() ints.
+__device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t *smem) {
+    WfLds L;
+    wf_lds(sh.E, sh.R, sh.pcap, smem, &L);
+    int *const s_T = L.T, *const s_cum = L.cum, *const s_ovpre = L.ovpre, *const s_nzpre = L.nzpre;
+    int *const s_ovlist = L.ovlist, *const s_listE = L.listE, *const s_keep = L.keep, *const s_O = L.O;
+    int *const s_D = L.D, *const s_Dpre = L.Dpre, *const s_dbeg = L.dbeg, *const s_dend = L.dend;
+    int *const s_nzlo = L.nzlo, *const s_ppre = L.ppre, *const s_w = L.w;
+    int &s_status = L.scal[0], &s_maxT = L.scal[1];
 
     const int tid = threadIdx.x;
     const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
@@ -398,6 +485,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
         p.list_rank[q] = r;
         p.list_b[q] = b;
         p.piece_js[q] = js - s_ovpre[e];  // first overflow index of the piece within its expert
+        p.pslot[q] = r * SK + start;
+        p.pcnt[q] = je - js;
         p.seg_ptr[(int64_t)r * sp + G + b] = start;
         p.seg_expert[(int64_t)r * se + G + b] = e;
         s_listE[q] = e;
@@ -418,6 +507,11 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
     solve_tail(sh, p, totNZ, &s_status, &s_maxT);
 }
 
+__global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
+    extern __shared__ int32_t smem[];
+    solve_waterfill(sh, p, smem);
+}
+
 // ---------------------------------------------------------------- k_solve_bounded
 // The plan that keeps at most B duplicates per rank where it can: an overloaded
 // rank overflows its largest experts first (T descending, then id); deficit ranks
@@ -434,7 +528,6 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
 // maximum reductions over the overflows, which wave 0 holds in registers
 // (kMaxE / 64 per lane): two when (rows, id) packs into one 31-bit key, three
 // otherwise.
-constexpr int kMaxPieces = kMaxE + kMaxR;
 constexpr int kItemsPerLane = kMaxE / 64;
 
 // Maximum over the 64 lanes, in every lane: DPP shifts inside each 16-lane row,
@@ -558,20 +651,18 @@ __device__ __forceinline__ int place_pieces(const PlaceArgs &a, bool packed) {
     return packed ? place_pieces<NS, true>(a) : place_pieces<NS, false>(a);
 }
 
-__global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
-    __shared__ int s_T[kMaxE];
-    __shared__ int s_cum[kMaxE + 1];
-    __shared__ int s_kc[kMaxE + 1];   // exclusive prefix of kept rows
-    __shared__ int s_ov[kMaxE];       // overflow rows of each expert
-    __shared__ int s_xl[kMaxE];       // overflowing experts in id order
-    __shared__ int s_bin[kMaxR + 1], s_binD[kMaxR + 1], s_binK[kMaxR + 1];  // deficit ranks in fill order
-    __shared__ uint64_t s_bkey[kMaxR];  // fill-order key of each rank (0: no deficit)
-    __shared__ int s_keep[kMaxR], s_O[kMaxR], s_D[kMaxR];
-    __shared__ int s_nd[kMaxR], s_first[kMaxR], s_fill[kMaxR];
-    __shared__ int s_pe[kMaxPieces], s_pr[kMaxPieces], s_pstart[kMaxPieces], s_pcnt[kMaxPieces];
-    __shared__ int s_pjj[kMaxPieces], s_pkey[kMaxPieces], s_skey[kMaxPieces];
-    __shared__ int s_w[(kSolveThreads / 64 + 1) * 4];
-    __shared__ int s_status, s_maxT, s_np, s_err;
+// One 1024-thread workgroup; smem holds bd_lds() ints.
+__device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *smem) {
+    BdLds L;
+    bd_lds(sh.E, sh.R, sh.pcap, smem, &L);
+    uint64_t *const s_bkey = L.bkey;
+    int *const s_T = L.T, *const s_cum = L.cum, *const s_kc = L.kc, *const s_ov = L.ov, *const s_xl = L.xl;
+    int *const s_bin = L.bin, *const s_binD = L.binD, *const s_binK = L.binK, *const s_keep = L.keep;
+    int *const s_O = L.O, *const s_D = L.D, *const s_nd = L.nd, *const s_first = L.first;
+    int *const s_fill = L.fill, *const s_pe = L.pe, *const s_pr = L.pr, *const s_pstart = L.pstart;
+    int *const s_pcnt = L.pcnt, *const s_pjj = L.pjj, *const s_pkey = L.pkey, *const s_skey = L.skey;
+    int *const s_w = L.w;
+    int &s_status = L.scal[0], &s_maxT = L.scal[1], &s_np = L.scal[2], &s_err = L.scal[3];
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
     const int E = sh.E, R = sh.R, G = sh.G, B = sh.B;
@@ -634,7 +725,7 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
 
     // 2. placement (wave 0), with as many register slots per lane as the overflows need
     if (w == 0) {
-        PlaceArgs a{n_items, n_bins, B, min(kMaxPieces, sh.pcap), s_xl, s_ov, s_bin, s_binD, s_binK,
+        PlaceArgs a{n_items, n_bins, B, sh.pcap, s_xl, s_ov, s_bin, s_binD, s_binK,
                     s_first, s_nd, s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj};
         const int nslots = (n_items + 63) >> 6;
         const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
@@ -693,6 +784,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
         p.list_rank[pos] = s_pr[q];
         p.list_b[pos] = q - s_first[s_pr[q]];
         p.piece_js[pos] = s_pjj[q];
+        p.pslot[pos] = s_pr[q] * sh.SK + s_pstart[q];
+        p.pcnt[pos] = s_pcnt[q];
     }
     __syncthreads();
     // CSR over experts: pieces of expert e are the keys in [e*R, (e+1)*R)
@@ -707,82 +800,118 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
     solve_tail(sh, p, n_items, &s_status, &s_maxT);
 }
 
-// ---------------------------------------------------------------- k_assign
+__global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
+    extern __shared__ int32_t smem[];
+    solve_bounded(sh, p, smem);
+}
+
+// ---------------------------------------------------------------- assign
 // Wave w of the tile takes entries [w*256, w*256 + 256) as kChunks chunks of 64,
 // lane l holding entry w*256 + c*64 + l of chunk c. Both plans place entries the
 // same way: an entry's position among its expert's entries (token, then k order)
 // below kept[e] is a home row from koff[e] on; position kept[e] + jj is overflow
 // row jj of the expert, in the one piece whose range [jj0, jj0 + count) holds it.
-// LDS of k_assign, sized to the problem (ints): see the carve-up below.
-inline size_t assign_lds_bytes(const PlanShape &sh) {
-    return sizeof(int32_t) * ((size_t)(kAssignWaves / 2) * sh.E + 3 * (size_t)sh.E + 1 +
-                              3 * (size_t)sh.pcap + (size_t)sh.R + 1);
+//
+// LDS (ints): s_pos, the per-wave counts and then running positions of every
+// expert (kAssignWaves / 2 * E; waves 2m and 2m+1 share a word, low and high 16
+// bits -- a tile has at most 4096 entries, so a half never carries into the
+// other), then the plan tables the placement reads.
+struct AsgTables {
+    int32_t *tbase;    // entries of e in earlier tiles
+    int32_t *kept;     // entries of e kept at home
+    int32_t *kslot;    // first home slot of e
+    int32_t *dup_ptr;  // pieces of e: [dup_ptr[e], dup_ptr[e+1])
+    int32_t *pjj;      // first overflow row of each piece within its expert
+    int32_t *pcnt;     // rows of each piece
+    int32_t *pslot;    // first slot of each piece
+    int32_t *upre;     // R + 1: exclusive prefix of empty slots per rank
+};
+
+__host__ __device__ inline int asg_tables(int E, int R, int pcap, int32_t *base, AsgTables *o) {
+    LdsCarve c{base, 0};
+    AsgTables t;
+    t.tbase = c.take(E);
+    t.kept = c.take(E);
+    t.kslot = c.take(E);
+    t.dup_ptr = c.take(E + 1);
+    t.pjj = c.take(pcap);
+    t.pcnt = c.take(pcap);
+    t.pslot = c.take(pcap);
+    t.upre = c.take(R + 1);
+    if (o) *o = t;
+    return c.off;
 }
 
-// Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
-// compiler budget scalar registers for that (the plan pointers would otherwise
-// hold enough of them to allow only one).
-__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
-    const int tile = blockIdx.x, tid = threadIdx.x;
-    const int lane = lane_id(), w = tid >> 6;
-    const int E = sh.E, R = sh.R, SK = sh.SK;
-    extern __shared__ int32_t smem[];
-    // Per-wave counts, then running positions relative to the tile's base, of
-    // waves 2m (low 16 bits) and 2m+1 (high 16 bits) of every expert: s_pos[m*E + e].
-    // A tile has at most 4096 entries, so a half never carries into the other.
-    uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
-    int32_t *s_tbase = smem + (kAssignWaves / 2) * E;  // entries of e in earlier tiles
-    int32_t *s_kept = s_tbase + E;                      // entries of e kept at home
-    int32_t *s_kslot = s_kept + E;                      // first home slot of e
-    int32_t *s_dup_ptr = s_kslot + E;                   // pieces of e: [s_dup_ptr[e], [e+1])
-    int32_t *s_pjj = s_dup_ptr + E + 1;                 // first overflow row of each piece
-    int32_t *s_pcnt = s_pjj + sh.pcap;                  // rows of each piece
-    int32_t *s_pslot = s_pcnt + sh.pcap;                // first slot of each piece
-    int32_t *s_upre = s_pslot + sh.pcap;                // R + 1
-    const int tok0 = tile * sh.tile_tokens;
-    const int n = min(sh.tile_tokens, sh.n_tok - tok0) * sh.K;
-    const int64_t a0 = (int64_t)tok0 * sh.K;
-    const int P = p.n_list[0];
+__host__ __device__ inline int pos_ints(const PlanShape &sh) { return (kAssignWaves / 2) * sh.E; }
 
-    // loads first, all in flight: this wave's ids, then one table element per thread
-    int idv[kChunks];
+inline size_t assign_lds_bytes(const PlanShape &sh) {
+    return sizeof(int32_t) * (size_t)(pos_ints(sh) + asg_tables(sh.E, sh.R, sh.pcap, nullptr, nullptr));
+}
+
+struct Tile {
+    int tile;   // index of the tile
+    int n;      // entries in it
+    int64_t a0; // its first entry
+};
+
+__device__ __forceinline__ Tile tile_of(const PlanShape &sh, int tile) {
+    const int tok0 = tile * sh.tile_tokens;
+    return Tile{tile, min(sh.tile_tokens, sh.n_tok - tok0) * sh.K, (int64_t)tok0 * sh.K};
+}
+
+__device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, const Tile &t,
+                                         int (&idv)[kChunks]) {
+    const int w = threadIdx.x >> 6, lane = lane_id();
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         const int i = w * (kChunks * 64) + c * 64 + lane;
-        idv[c] = i < n ? ids[a0 + i] : -1;
+        idv[c] = i < t.n ? ids[t.a0 + i] : -1;
     }
-    int gbase = 0;
+}
+
+// The plan tables the placement needs, into LDS (no barrier). With TBASE,
+// tile_counts[tile] must already hold the exclusive prefix over earlier tiles;
+// without it, the caller fills t.tbase.
+template <bool TBASE>
+__device__ __forceinline__ void load_tables(const PlanShape &sh, const PlanPtrs &p, int tile,
+                                            const AsgTables &t) {
+    const int tid = threadIdx.x, E = sh.E, R = sh.R;
     if (tid < E) {
-        gbase = p.tile_counts[(int64_t)tile * E + tid];
-        s_kept[tid] = p.kept[tid];
-        s_kslot[tid] = (tid / sh.G) * SK + p.koff[tid];
-        s_dup_ptr[tid] = p.dup_ptr[tid];
+        if (TBASE) t.tbase[tid] = p.tile_counts[(int64_t)tile * E + tid];
+        t.kept[tid] = p.kept[tid];
+        t.kslot[tid] = (tid / sh.G) * sh.SK + p.koff[tid];
+        t.dup_ptr[tid] = p.dup_ptr[tid];
     }
-    if (tid < R) s_upre[tid] = p.upre[tid];
+    if (tid < R) t.upre[tid] = p.upre[tid];
     if (tid == 0) {
-        s_dup_ptr[E] = p.dup_ptr[E];
-        s_upre[R] = p.upre[R];
+        t.dup_ptr[E] = p.dup_ptr[E];
+        t.upre[R] = p.upre[R];
     }
-    for (int q = tid; q < P; q += kAssignThreads) {
-        const int64_t rb = (int64_t)p.list_rank[q] * sh.dcap + p.list_b[q];
-        s_pjj[q] = p.piece_js[q];
-        s_pcnt[q] = p.dup_count[rb];
-        s_pslot[q] = p.list_rank[q] * SK + p.dup_start[rb];
+    // the whole piece table, no dependent loads: only entries below the list
+    // length are ever looked up (through dup_ptr)
+    for (int q = tid; q < sh.pcap; q += kAssignThreads) {
+        t.pjj[q] = p.piece_js[q];
+        t.pcnt[q] = p.pcnt[q];
+        t.pslot[q] = p.pslot[q];
     }
+}
+
+__device__ __forceinline__ void zero_pos(const PlanShape &sh, uint32_t *s_pos) {
 #pragma unroll
     for (int m = 0; m < kAssignWaves / 2; ++m)
-        if (tid < E) s_pos[m * E + tid] = 0u;
-    __syncthreads();
-    const int half = (w & 1) * 16;
+        if ((int)threadIdx.x < sh.E) s_pos[m * sh.E + threadIdx.x] = 0u;
+}
 
-    // pass 1: which lanes of each chunk hold the same id (bit-sliced ballots);
-    // the lowest lane of each group adds the group's size to the wave's count
-    uint64_t same[kChunks];
+// Pass 1: which lanes of each chunk hold the same id (bit-sliced ballots); the
+// lowest lane of each group adds the group's size to the wave's count.
+__device__ __forceinline__ void count_waves(const PlanShape &sh, const int (&idv)[kChunks],
+                                            uint64_t (&same)[kChunks], uint32_t *s_pos) {
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int half = (w & 1) * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         const int e = idv[c];
-        const bool valid = e >= 0 && e < E;
+        const bool valid = e >= 0 && e < sh.E;
         uint64_t mask = __ballot(valid);
 #pragma unroll
         for (int bit = 0; bit < kMaxIdBits; ++bit) {
@@ -794,51 +923,60 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
         }
         same[c] = mask;
         if (valid && lane == __ffsll((unsigned long long)mask) - 1)
-            atomicAdd(&s_pos[(w >> 1) * E + e], (uint32_t)__popcll(mask) << half);
+            atomicAdd(&s_pos[(w >> 1) * sh.E + e], (uint32_t)__popcll(mask) << half);
     }
-    __syncthreads();
-    // running positions: earlier waves of this tile, relative to the tile base
-    if (tid < E) {
-        uint32_t run = 0;
+}
+
+// Per-wave counts -> running positions relative to the tile base (earlier waves
+// of this tile); returns the tile's count of expert threadIdx.x (0 beyond E).
+__device__ __forceinline__ int running_positions(const PlanShape &sh, uint32_t *s_pos) {
+    uint32_t run = 0;
+    if ((int)threadIdx.x < sh.E) {
 #pragma unroll
         for (int m = 0; m < kAssignWaves / 2; ++m) {
-            const uint32_t word = s_pos[m * E + tid];
+            const uint32_t word = s_pos[m * sh.E + threadIdx.x];
             const uint32_t lo = word & 0xffffu, hi = word >> 16;
-            s_pos[m * E + tid] = run | ((run + lo) << 16);
+            s_pos[m * sh.E + threadIdx.x] = run | ((run + lo) << 16);
             run += lo + hi;
         }
-        s_tbase[tid] = gbase;
     }
-    __syncthreads();
+    return (int)run;
+}
 
-    // pass 2: chunks in order; position = wave's running position + lanes below
-    // with the same id; then the slot
+// Pass 2: chunks in order; position = wave's running position + lanes below with
+// the same id; then the slot, dst and src.
+__device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
+                                              const int (&idv)[kChunks],
+                                              const uint64_t (&same)[kChunks], uint32_t *s_pos,
+                                              const AsgTables &tb) {
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int half = (w & 1) * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         const int e = idv[c];
         const int i = w * (kChunks * 64) + c * 64 + lane;
-        const bool valid = e >= 0 && e < E;
+        const bool valid = e >= 0 && e < sh.E;
         if (valid) {
             const uint64_t mask = same[c];
             const int below = __builtin_amdgcn_mbcnt_hi(
                 (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-            const int rel = (int)((s_pos[(w >> 1) * E + e] >> half) & 0xffffu);
-            const int pos = s_tbase[e] + rel + below;
+            const int rel = (int)((s_pos[(w >> 1) * sh.E + e] >> half) & 0xffffu);
+            const int pos = tb.tbase[e] + rel + below;
             // the wave's read above is issued before this add (LDS keeps a wave's
             // operations in order); the other wave of the word only adds to its half
             if (lane == 63 - __clzll((long long)mask))
-                atomicAdd(&s_pos[(w >> 1) * E + e], (uint32_t)__popcll(mask) << half);
-            const int kept = s_kept[e];
+                atomicAdd(&s_pos[(w >> 1) * sh.E + e], (uint32_t)__popcll(mask) << half);
+            const int kept = tb.kept[e];
             int slot = -1;
             if (pos < kept) {
-                slot = s_kslot[e] + pos;
+                slot = tb.kslot[e] + pos;
             } else {
                 const int jj = pos - kept;
-                const int q1 = s_dup_ptr[e + 1];
-                for (int q = s_dup_ptr[e]; q < q1; ++q) {
-                    const int d = jj - s_pjj[q];
-                    if ((unsigned)d < (unsigned)s_pcnt[q]) {
-                        slot = s_pslot[q] + d;
+                const int q1 = tb.dup_ptr[e + 1];
+                for (int q = tb.dup_ptr[e]; q < q1; ++q) {
+                    const int d = jj - tb.pjj[q];
+                    if ((unsigned)d < (unsigned)tb.pcnt[q]) {
+                        slot = tb.pslot[q] + d;
                         break;
                     }
                 }
@@ -846,18 +984,23 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
             // A correct plan always lands inside the buffer; the guard only keeps a
             // broken invariant from turning into a wild store.
             if ((unsigned)slot < (unsigned)sh.n_ent) {
-                p.dst[a0 + i] = slot;
-                p.src[slot] = (int32_t)(a0 + i);
+                p.dst[t.a0 + i] = slot;
+                p.src[slot] = (int32_t)(t.a0 + i);
             } else {
-                p.dst[a0 + i] = -1;
+                p.dst[t.a0 + i] = -1;
             }
-        } else if (i < n) {
-            p.dst[a0 + i] = -1;
+        } else if (i < t.n) {
+            p.dst[t.a0 + i] = -1;
         }
     }
+}
 
-    // Tails of the plan tables and unfilled slots, spread over the whole grid.
-    const int gt = blockIdx.x * kAssignThreads + tid;
+// Tails of the plan tables and unfilled slots, spread over the whole grid.
+__device__ __forceinline__ void plan_tails(const PlanShape &sh, const PlanPtrs &p,
+                                           const int32_t *s_upre) {
+    const int R = sh.R, SK = sh.SK;
+    const int P = p.n_list[0];
+    const int gt = blockIdx.x * kAssignThreads + threadIdx.x;
     const int gn = gridDim.x * kAssignThreads;
     const int sp = sh.G + sh.dcap + 1, se = sh.G + sh.dcap;
     const int ntab = R * sh.dcap;  // < 2^31: R, dcap <= 1024
@@ -887,10 +1030,290 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     }
 }
 
+// ---------------------------------------------------------------- k_assign
+// Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
+// compiler budget scalar registers for that (the plan pointers would otherwise
+// hold enough of them to allow only one).
+__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
+    extern __shared__ int32_t smem[];
+    uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
+    AsgTables tb;
+    asg_tables(sh.E, sh.R, sh.pcap, smem + pos_ints(sh), &tb);
+    const Tile t = tile_of(sh, blockIdx.x);
+
+    // loads first, all in flight: this wave's ids, then the tables
+    int idv[kChunks];
+    load_ids(ids, t, idv);
+    load_tables<true>(sh, p, t.tile, tb);
+    zero_pos(sh, s_pos);
+    __syncthreads();
+    uint64_t same[kChunks];
+    count_waves(sh, idv, same, s_pos);
+    __syncthreads();
+    running_positions(sh, s_pos);
+    __syncthreads();
+    place_entries(sh, p, t, idv, same, s_pos, tb);
+    plan_tails(sh, p, tb.upre);
+}
+
+// ---------------------------------------------------------------- k_plan_fused
+// The whole water-fill plan in one launch, for problems whose tiles all fit on
+// the GPU at once (the host checks that before choosing this kernel). The
+// bounded plan always takes four launches: its solve inlined here would not fit
+// the 128 registers a lane of a 16-wave workgroup may hold. One 1024-thread
+// workgroup per tile:
+//   1. it loads its ids (kept in registers to the end) and publishes its expert
+//      histogram;
+//   2. workgroup 0 waits for every tile, sums T over the tiles, runs the solve,
+//      publishes the plan tables and only then takes its own per-wave counts,
+//      in-chunk matches (the ballots of pass 1) and status bits; the others take
+//      theirs while the plan is being made, then wait for it;
+//   3. every workgroup adds its status bits, sums its tile's base over the
+//      earlier tiles and places its own entries.
+// tile_counts keeps each tile's own counts here (no scan in place).
+// Synchronisation is through ws_sync: [0] a generation number, [1 + t] tile t's
+// arrival. Each call reads the generation g; a tile arrives by storing g + 1,
+// and workgroup 0 releases by storing g + 1 as the new generation. Values left
+// by earlier calls are at most g, so any starting contents work. Every wait is
+// bounded: on time-out MOONEP_STATUS_SYNC_TIMEOUT is raised and every wave
+// still exits.
+constexpr int kFusedMaxTiles = 64;
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
+constexpr uint32_t kSpinLimit = 1u << 21;
+
+__device__ __forceinline__ uint64_t load_acquire(const uint64_t *a) {
+    return __hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_release(uint64_t *a, uint64_t v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polling reads: coherent at device scope but without the cache invalidation of
+// an acquire (one acquire fence follows the wait instead).
+__device__ __forceinline__ uint64_t load_relaxed(const uint64_t *a) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of counts[t][e] over tiles t in [0, n_tiles), n_tiles <= kFusedMaxTiles:
+// 32 independent loads in flight per round.
+__device__ __forceinline__ int sum_tiles(const int32_t *counts, int E, int e, int n_tiles) {
+    int sum = 0;
+    for (int t0 = 0; t0 < n_tiles; t0 += 32) {
+        int v[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) v[u] = t0 + u < n_tiles ? counts[(int64_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) sum += v[u];
+    }
+    return sum;
+}
+
+inline size_t fused_lds_bytes(const PlanShape &sh) {
+    const int solve = wf_lds(sh.E, sh.R, sh.pcap, nullptr, nullptr);
+    const int tables = asg_tables(sh.E, sh.R, sh.pcap, nullptr, nullptr);
+    const int region = max(max(solve, tables), sh.E + kTileEntries);  // histogram + ids
+    return sizeof(int32_t) * (size_t)(pos_ints(sh) + 4 + region);
+}
+
+// This tile's status bits: invalid ids, and ids repeated within a token (valid
+// ones only). When K divides 64 a token's K entries are K aligned lanes of one
+// chunk, and the ballot masks already say which of them hold the same id;
+// otherwise the tile's ids are compared in LDS (s_ids).
+__device__ __forceinline__ int tile_status_bits(const PlanShape &sh, const Tile &t,
+                                                const int (&idv)[kChunks],
+                                                const uint64_t (&same)[kChunks],
+                                                const int32_t *s_ids) {
+    const int w = threadIdx.x >> 6, lane = lane_id(), K = sh.K;
+    const bool aligned = (64 % K) == 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint64_t group = (K == 64 ? ~0ull : ((1ull << K) - 1ull)) << (lane - lane % K);
+    int st = 0;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int i = w * (kChunks * 64) + c * 64 + lane;
+        const int e = idv[c];
+        if (i < t.n) {
+            if (e < 0 || e >= sh.E) {
+                st |= MOONEP_STATUS_BAD_ID;
+            } else if (aligned) {
+                if (same[c] & group & below) st |= MOONEP_STATUS_REPEAT_ID;
+            } else {
+                const int k = i % K;
+                for (int k2 = 1; k2 <= k; ++k2)
+                    if (s_ids[i - k2] == e) st |= MOONEP_STATUS_REPEAT_ID;
+            }
+        }
+    }
+    return st;
+}
+
+__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_plan_fused(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p, uint64_t *sync) {
+    extern __shared__ int32_t smem[];
+    const int tid = threadIdx.x, E = sh.E;
+    uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);  // kept from the ballots to step 3
+    int32_t *s_misc = smem + pos_ints(sh);                 // [0] status bits, [1] time-out
+    int32_t *region = s_misc + 4;                          // histogram and ids, solve, tables
+    int32_t *s_ids = region + E;                           // the tile's ids (kTileEntries)
+    const Tile t = tile_of(sh, blockIdx.x);
+
+    // 1. this tile's expert counts, published as soon as they are known
+    __shared__ uint64_t s_gen;
+    if (tid == 0) {
+        s_gen = load_acquire(sync);
+        s_misc[0] = 0;
+        s_misc[1] = 0;
+    }
+    int idv[kChunks];
+    load_ids(ids, t, idv);
+    for (int e = tid; e < E; e += kAssignThreads) region[e] = 0;
+    __syncthreads();
+    {
+        const int w = tid >> 6, lane = lane_id();
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int i = w * (kChunks * 64) + c * 64 + lane;
+            if (i < t.n) {
+                s_ids[i] = idv[c];
+                if (idv[c] >= 0 && idv[c] < E) atomicAdd(&region[idv[c]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < E) p.tile_counts[(int64_t)t.tile * E + tid] = region[tid];
+    if (tid == 0) p.tile_status[t.tile] = 0;  // this tile's bits reach the status in step 3
+    const uint64_t g = s_gen;
+    __syncthreads();
+    if (tid == 0) store_release(&sync[1 + t.tile], g + 1);
+
+    // 2. the plan tables: workgroup 0 solves while the others take their per-wave
+    // counts, in-chunk matches and status bits, then wait for the plan
+    uint64_t same[kChunks];
+    if (t.tile == 0) {
+        int late = 0;
+        if (tid < sh.n_tiles) {
+            uint32_t spins = 0;
+            while (load_relaxed(&sync[1 + tid]) != g + 1) {
+                if (++spins >= kSpinLimit) {
+                    late = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (__syncthreads_or(late) && tid == 0) p.tile_status[0] = MOONEP_STATUS_SYNC_TIMEOUT;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // T from the tiles' counts (each tile's own base is summed in step 3)
+        if (tid < E) p.T[tid] = sum_tiles(p.tile_counts, E, tid, sh.n_tiles);
+        __syncthreads();
+        solve_waterfill(sh, p, region);
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) store_release(sync, g + 1);
+        // this tile's own matches, after the release: the ids are read again so
+        // that nothing of them stays in registers across the solve
+        load_ids(ids, t, idv);
+        for (int i = tid; i < t.n; i += kAssignThreads) s_ids[i] = ids[t.a0 + i];
+        zero_pos(sh, s_pos);
+        __syncthreads();
+        count_waves(sh, idv, same, s_pos);
+        const int st = tile_status_bits(sh, t, idv, same, s_ids);
+        if (st) atomicOr(&s_misc[0], st);
+        __syncthreads();
+    } else {
+        zero_pos(sh, s_pos);
+        __syncthreads();
+        count_waves(sh, idv, same, s_pos);
+        {
+            const int st = tile_status_bits(sh, t, idv, same, s_ids);
+            if (st) atomicOr(&s_misc[0], st);
+        }
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (load_relaxed(sync) == g) {
+                if (++spins >= kSpinLimit) {
+                    s_misc[1] = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        if (s_misc[1]) {  // the plan never came: leave this tile's entries alone
+            if (tid == 0) atomicOr(p.status, MOONEP_STATUS_SYNC_TIMEOUT);
+            return;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+
+    // 3. place this tile's entries; the tile's base is the sum over earlier tiles
+    if (tid == 0 && s_misc[0]) atomicOr(p.status, s_misc[0]);
+    AsgTables tb;
+    asg_tables(sh.E, sh.R, sh.pcap, region, &tb);
+    load_tables<false>(sh, p, t.tile, tb);
+    if (tid < E) tb.tbase[tid] = sum_tiles(p.tile_counts, E, tid, t.tile);
+    running_positions(sh, s_pos);
+    __syncthreads();
+    place_entries(sh, p, t, idv, same, s_pos, tb);
+    plan_tails(sh, p, tb.upre);
+}
+
+}  // namespace
+
+namespace {
+
+hipError_t allow_lds(const void *kernel, size_t lds) {
+    if (lds <= 65536) return hipSuccess;  // within the default dynamic LDS limit of a launch
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+// Workgroups of the fused kernel the current device holds at once with lds bytes
+// of LDS each.
+int fused_resident(const void *kernel, size_t lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAssignThreads, lds) !=
+        hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+// MOONEP_PLAN_LAUNCH=fused asks for the water-fill's one-launch form (an error
+// where the shape cannot take it); otherwise four launches. At the decode shape
+// the two forms took the same time (29.6 against 30.4 us of kernel time): the
+// two hand-overs between workgroups cost what the three kernel boundaries do.
+// The bounded plan always takes four launches.
+enum class Launch { Auto, Multi, Fused };
+
+Launch launch_mode() {
+    const char *v = getenv("MOONEP_PLAN_LAUNCH");
+    if (v && strcmp(v, "multi") == 0) return Launch::Multi;
+    if (v && strcmp(v, "fused") == 0) return Launch::Fused;
+    return Launch::Auto;
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st) {
+    const Launch mode = launch_mode();
+    if (!bounded && sh.n_tiles <= kFusedMaxTiles && mode == Launch::Fused) {
+        const void *kf = (const void *)k_plan_fused;
+        const size_t lds = fused_lds_bytes(sh);
+        // a shape whose LDS the device cannot give one workgroup is not eligible
+        if (lds <= kMaxLdsBytes && allow_lds(kf, lds) == hipSuccess &&
+            fused_resident(kf, lds) >= sh.n_tiles) {
+            hipLaunchKernelGGL(k_plan_fused, dim3(sh.n_tiles), dim3(kAssignThreads), lds, st, ids, sh,
+                               p, p.sync);
+            return hipGetLastError();
+        }
+    }
+    if (mode == Launch::Fused && !bounded) return hipErrorInvalidConfiguration;
     const dim3 tiles(sh.n_tiles);
 #define MOONEP_COUNT(KM)                                                                    \
     hipLaunchKernelGGL(k_count<KM>, tiles, dim3(kPlanThreads), 0, st, ids, sh, p.tile_counts, \
@@ -905,14 +1328,14 @@ hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &
 #undef MOONEP_COUNT
     hipLaunchKernelGGL(k_scan, dim3((sh.E + 63) / 64), dim3(kScanThreads), 0, st, sh,
                        p.tile_counts, p.T);
-    if (bounded) hipLaunchKernelGGL(k_solve_bounded, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
-    else hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), 0, st, sh, p);
+    const size_t slds = solve_lds_bytes(sh, bounded);
+    hipError_t e = allow_lds(bounded ? (const void *)k_solve_bounded : (const void *)k_solve, slds);
+    if (e != hipSuccess) return e;
+    if (bounded) hipLaunchKernelGGL(k_solve_bounded, dim3(1), dim3(kSolveThreads), slds, st, sh, p);
+    else hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), slds, st, sh, p);
     const size_t lds = assign_lds_bytes(sh);
-    if (lds > 65536) {  // beyond the default dynamic LDS limit of a launch
-        const hipError_t e = hipFuncSetAttribute((const void *)k_assign,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    e = allow_lds((const void *)k_assign, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_assign, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
     return hipGetLastError();
 }
