@@ -1,0 +1,99 @@
+"""CPU tests of bench.py's own logic: the counter-CSV reduction behind
+roofline.traffic, the algorithmic byte counts, and the one-GPU contract."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+          "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+          "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+          "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for did, name, kib in rows:
+            r = {k: 0 for k in FIELDS}
+            r.update({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter,
+                      "Counter_Value": kib})
+            w.writerow(r)
+
+
+def test_traffic_from_pmc_scales_by_the_calibration_copy(tmp_path):
+    """Two calls (steps 1 + warm-up 1): dispatch = 2 launches per call, 1000 KiB
+    each by the counter; a copy kernel before the library kernels is ignored, the
+    first copy after the last library kernel is the calibration."""
+    steps, warmup = 1, 1
+    disp = "void moonep::(anonymous namespace)::k_dispatch<14, 3>(HIP_vector_type<unsigned int, 4u> const*)"
+    comb = "void moonep::(anonymous namespace)::k_combine<14, true, true, false>(int)"
+    plan = "moonep::(anonymous namespace)::k_assign(int const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    cal_bytes = bench.COPY_CAL_BYTES
+    rows_f = [(1, copy, 5.0)]  # an input upload: not the calibration
+    rows_w = [(1, copy, 7.0)]
+    did = 2
+    for _ in range(steps + warmup):
+        for name, f_kib, w_kib in ((plan, 3.0, 4.0), (disp, 1000.0, 2000.0), (disp, 1000.0, 2000.0),
+                                   (comb, 4000.0, 100.0)):
+            rows_f.append((did, name, f_kib))
+            rows_w.append((did, name, w_kib))
+            did += 1
+    # the copy reads half of what it moves by this counter, writes all of it
+    rows_f.append((did, copy, cal_bytes / 1024.0 / 2.0))
+    rows_w.append((did, copy, cal_bytes / 1024.0))
+    rows_f.append((did + 1, copy, 1.0))  # later copies are not the calibration
+    rows_w.append((did + 1, copy, 1.0))
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(fp, "FETCH_SIZE", rows_f)
+    _write_csv(wp, "WRITE_SIZE", rows_w)
+    rec = bench.traffic_from_pmc(str(fp), str(wp), steps, warmup, "cmd")
+    assert rec["fetch_size_scale"] == pytest.approx(2.0)
+    assert rec["write_size_scale"] == pytest.approx(1.0)
+    d = rec["ops"]["dispatch"]
+    assert d["fetch_size_bytes_per_call"] == pytest.approx(2 * 1000.0 * 1024 * 2.0)
+    assert d["write_size_bytes_per_call"] == pytest.approx(2 * 2000.0 * 1024)
+    assert d["hbm_bytes_per_call"] == pytest.approx(d["fetch_size_bytes_per_call"] +
+                                                    d["write_size_bytes_per_call"])
+    assert rec["ops"]["combine"]["fetch_size_bytes_per_call"] == pytest.approx(4000.0 * 1024 * 2.0)
+    assert rec["ops"]["plan"]["write_size_bytes_per_call"] == pytest.approx(4.0 * 1024)
+    assert d["source_hash"] == bench.kernel_source_hash(bench.OP_SOURCES["dispatch"])
+
+
+def test_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):
+    path = tmp_path / "t.json"
+    good = bench.kernel_source_hash(bench.OP_SOURCES["dispatch"])
+    path.write_text(json.dumps({"ops": {"dispatch": {"source_hash": good, "hbm_bytes_per_call": 5.0},
+                                        "combine": {"source_hash": "stale", "hbm_bytes_per_call": 6.0}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_PATH", str(path))
+    assert bench.traffic_for("dispatch") == 5.0
+    assert bench.traffic_for("combine") is None
+
+
+def test_algorithmic_bytes_by_hand():
+    wl = W.WORKLOADS["k3"]
+    row = 7168 * 2
+    n_tok, n_ent = 32 * 4096, 32 * 4096 * 16
+    b = bench.algorithmic_bytes(wl, n_mat=112, n_xm=94)
+    assert b["dispatch"] == n_ent * row + n_tok * row + 4 * n_ent == 31_952_207_872
+    assert b["combine"] == n_ent * row + n_tok * row + 8 * n_ent == 31_960_596_480
+    block = 3 * 7168 * 512
+    assert b["replicate"] == 2 * 112 * block * 2 == 4_932_501_504
+    assert b["reduce"] == (112 + 2 * 94) * block * 4 == 13_212_057_600
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
