@@ -61,8 +61,7 @@ def algorithmic_bytes(wl, n_mat, n_xm):
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
 
 # Library kernels behind each C-ABI call (one call may enqueue several launches).
-OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign",
-                       "k_plan_fused"),
+OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign"),
               "replicate": ("k_replicate",),
               "dispatch": ("k_dispatch",), "combine": ("k_combine",), "reduce": ("k_reduce",)}
 # (k_combine also serves the backward of dispatch, so traffic is only summed for

@@ -53,12 +53,9 @@ enum {
     MOONEP_STATUS_BAD_ID = 1,    /* an id outside [0, E): that entry is dropped (dst = -1) */
     MOONEP_STATUS_REPEAT_ID = 2, /* one token names the same expert twice; the plan is
                                     still well defined, ties broken by (token, k)        */
-    MOONEP_STATUS_OVER_B = 4,    /* some rank needs more than B duplicates; the plan is
+    MOONEP_STATUS_OVER_B = 4     /* some rank needs more than B duplicates; the plan is
                                     complete, but only duplicates b < B have a slot in
                                     replicate / reduce                                  */
-    MOONEP_STATUS_SYNC_TIMEOUT = 8 /* the one-launch plan gave up waiting for its own
-                                    workgroups (the GPU was shared so heavily that they
-                                    could not all run); the plan is not valid           */
 };
 
 /*
@@ -122,7 +119,7 @@ typedef struct moonep_layout {
     int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
     int64_t n_list, list_expert, list_rank, list_b, dup_ptr;
     int64_t ws_tile_counts, ws_tile_status, ws_mat_pre, ws_xlist, ws_n_x, ws_piece_js;
-    int64_t ws_kept, ws_koff, ws_upre, ws_sync, ws_pslot, ws_pcnt;
+    int64_t ws_kept, ws_koff, ws_upre, ws_pslot, ws_pcnt;
 } moonep_layout;
 
 /* Fills *out for dims. Pure host computation. Returns MOONEP_OK or
@@ -146,13 +143,8 @@ int moonep_plan_layout(const moonep_dims *dims, moonep_layout *out);
  * The result depends on the ids only (B only sets MOONEP_STATUS_OVER_B) and is
  * bit-for-bit deterministic.
  *
- * Launches: four kernels. With MOONEP_PLAN_LAUNCH=fused in the environment
- * (read on every call) the plan is one kernel instead, whose workgroups
- * synchronise through workspace words of plan_buf; that form needs ids that split
- * into at most 64 tiles of 4096 entries, all of whose workgroups fit on the
- * device at once (MOONEP_ERR_HIP otherwise), and gives the same plan. Neither
- * form needs the buffer initialised, but one plan buffer must not be used by two
- * calls that run at the same time.
+ * Four kernel launches. The plan buffer needs no initialisation; one plan buffer
+ * must not be used by two calls that run at the same time.
  */
 int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf, void *stream);
 
@@ -179,7 +171,7 @@ int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf
  *     ordered by (expert, rank).
  * A rank that still needs more than B duplicates sets MOONEP_STATUS_OVER_B, as in
  * moonep_plan. Bit-for-bit deterministic; the moves and backward entry points
- * take its plan unchanged. Always four kernels (MOONEP_PLAN_LAUNCH is ignored).
+ * take its plan unchanged.
  */
 int moonep_plan_bounded(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf,
                         void *stream);

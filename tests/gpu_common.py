@@ -1,7 +1,5 @@
 """Helpers of the GPU parity tests: run the HIP path through the C ABI and read
 results back for comparison with the oracle. Nothing here computes the method."""
-import contextlib
-import os
 import sys
 
 import numpy as np
@@ -18,25 +16,6 @@ def say(msg):
 
 def dims_for(td, R, E, K, S, B, H, dtype):
     return td.Dims(R, E, K, S, B, dtype, H)
-
-
-@contextlib.contextmanager
-def plan_launch(mode):
-    """Run the plan calls inside with MOONEP_PLAN_LAUNCH=mode ("fused": the
-    one-launch plan, an error where the shape cannot take it; "multi": four
-    kernels; None: chosen by shape)."""
-    old = os.environ.get("MOONEP_PLAN_LAUNCH")
-    if mode is None:
-        os.environ.pop("MOONEP_PLAN_LAUNCH", None)
-    else:
-        os.environ["MOONEP_PLAN_LAUNCH"] = mode
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("MOONEP_PLAN_LAUNCH", None)
-        else:
-            os.environ["MOONEP_PLAN_LAUNCH"] = old
 
 
 def run_plan(td, dims, ids_np, dev, plan_buf=None, bounded=False):

@@ -60,7 +60,7 @@ def test_layout(td, shape):
              "list_rank": 4 * lay.pcap, "list_b": 4 * lay.pcap, "dup_ptr": 4 * (E + 1),
              "ws_tile_counts": 4 * lay.n_tiles * E, "ws_tile_status": 4 * lay.n_tiles,
              "ws_mat_pre": 4 * (R + 1), "ws_xlist": 4 * E, "ws_n_x": 4,
-             "ws_piece_js": 4 * lay.pcap, "ws_kept": 4 * E, "ws_koff": 4 * E, "ws_upre": 4 * (R + 1), "ws_sync": 8 * (lay.n_tiles + 1),
+             "ws_piece_js": 4 * lay.pcap, "ws_kept": 4 * E, "ws_koff": 4 * E, "ws_upre": 4 * (R + 1),
              "ws_pslot": 4 * lay.pcap, "ws_pcnt": 4 * lay.pcap}
     spans = sorted((getattr(lay, k), getattr(lay, k) + v) for k, v in sizes.items())
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):

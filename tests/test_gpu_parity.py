@@ -6,10 +6,7 @@ compared bit for bit too, which is stricter than the 1e-5 relative bound the
 path promises (that bound is also asserted on the fp32 combine output).
 
 Both plans are covered: the water-fill (moonep_plan) and the plan bounded by B
-duplicates per rank (moonep_plan_bounded), each against its oracle; the
-water-fill in both of its forms: one kernel for shapes of at most 64 tiles
-("fused", required where a test names it, so the test fails if that path is
-not taken) and four kernels ("multi").
+duplicates per rank (moonep_plan_bounded), each against its oracle.
 
 Small shapes are compared element by element; they span several plan tiles with
 a ragged last tile and rows whose 16-byte chunk count does not fill the lanes.
@@ -24,8 +21,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, plan_launch, read_plan,
-                              run_plan, say)
+from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, read_plan, run_plan,
+                              say)
 from tests.invariants import check_plan
 
 pytestmark = pytest.mark.gpu
@@ -142,17 +139,14 @@ def _full_case(td, wl, ids, w, seed, bounded=False):
     return g
 
 
-# the water-fill in its one-launch and four-launch forms; the bounded plan has only the latter
-PLANS = pytest.mark.parametrize("bounded,launch", [(False, "fused"), (False, "multi"), (True, None)],
-                                ids=["waterfill-fused", "waterfill-multi", "bounded"])
+PLANS = pytest.mark.parametrize("bounded", [False, True], ids=["waterfill", "bounded"])
 
 
 @PLANS
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_small_shapes_elementwise(td, wl, bounded, launch):
+def test_small_shapes_elementwise(td, wl, bounded):
     ids, w = W.make_routing(wl, seed=3)
-    with plan_launch(launch):
-        _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
+    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
 
 
 def test_hand_worked_examples_on_gpu(td):
@@ -208,7 +202,7 @@ def test_bounded_hand_worked_examples_on_gpu(td):
 
 
 @PLANS
-def test_invalid_and_repeated_ids(td, bounded, launch):
+def test_invalid_and_repeated_ids(td, bounded):
     wl = _wl("bad_ids", 4, 32, 4, 1500, 4, 64, W.BF16, 2.0)
     rng = np.random.default_rng(17)
     ids, w = W.make_routing(wl, seed=5)
@@ -216,33 +210,29 @@ def test_invalid_and_repeated_ids(td, bounded, launch):
     w = w.reshape(-1)
     bad = rng.choice(ids.size, 40, replace=False)
     ids[bad] = rng.choice([-1, -100, wl.E, wl.E + 7], 40)
-    with plan_launch(launch):
-        g = _full_case(td, wl, ids, w, 5, bounded)
+    g = _full_case(td, wl, ids, w, 5, bounded)
     assert int(g["status"][0]) & 1
     ids2, w2 = W.make_routing(wl, seed=6)
     ids2 = ids2.reshape(-1, wl.K).copy()
     t = rng.choice(wl.n_tok, 25, replace=False)
     ids2[t, 2] = ids2[t, 0]
-    with plan_launch(launch):
-        g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6, bounded)
+    g = _full_case(td, wl, ids2.reshape(-1), w2.reshape(-1), 6, bounded)
     assert int(g["status"][0]) & 2
 
 
 @PLANS
-def test_extreme_skew_and_balance(td, bounded, launch):
+def test_extreme_skew_and_balance(td, bounded):
     # every token picks the same K experts, all homed on rank 0
     wl = _wl("one_hot_rank", 8, 64, 8, 1000, 8, 64, W.BF16, 0.0)
     ids = np.tile(np.arange(8, dtype=np.int32), wl.n_tok)
     w = np.full(ids.size, 1.0 / 8, np.float32)
-    with plan_launch(launch):
-        g = _full_case(td, wl, ids, w, 1, bounded)
+    g = _full_case(td, wl, ids, w, 1, bounded)
     assert int(g["n_dup"].sum()) > 0 and int(g["L"][0]) == wl.n_ent
     # perfectly balanced routing: no overflow, no duplicates
     wl = _wl("balanced", 4, 16, 4, 256, 2, 64, W.BF16, 0.0)
     ids = (np.arange(wl.n_ent) % wl.E).astype(np.int32)
     w = np.full(ids.size, 0.25, np.float32)
-    with plan_launch(launch):
-        g = _full_case(td, wl, ids, w, 2, bounded)
+    g = _full_case(td, wl, ids, w, 2, bounded)
     assert int(g["n_dup"].sum()) == 0 and float(g["maxvio"][0]) == 0.0
 
 
@@ -262,8 +252,7 @@ def test_identity_expert_mean_returns_hidden(td):
     assert torch.equal(out.view(torch.int16), hid.view(torch.int16))
 
 
-@pytest.mark.parametrize("launch", ["fused", "multi"])
-def test_deterministic_and_stream_ordered(td, launch):
+def test_deterministic_and_stream_ordered(td):
     wl = W.WORKLOADS["zipf"].replace(S=512)
     dims = _dims(td, wl)
     ids, _ = W.make_routing(wl, seed=1)
@@ -271,7 +260,7 @@ def test_deterministic_and_stream_ordered(td, launch):
     bufs = []
     for _ in range(3):
         pb = td.new_plan_buffer(dims, DEV)
-        with torch.cuda.stream(s), plan_launch(launch):
+        with torch.cuda.stream(s):
             ids_d = torch.from_numpy(ids).to(DEV, non_blocking=False)
             td.moonep_plan(dims, ids_d, pb, stream=s)
         bufs.append(pb)
@@ -282,8 +271,7 @@ def test_deterministic_and_stream_ordered(td, launch):
         assert_plan_equal(read_plan(td, dims, pb), a)
 
 
-@pytest.mark.parametrize("launch", ["fused", "multi"])
-def test_plan_buffer_reuse_across_shapes(td, launch):
+def test_plan_buffer_reuse_across_shapes(td):
     """A plan buffer first used for a larger problem gives the same plan for a
     smaller one (no stale state leaks into the result)."""
     big = _wl("big", 8, 64, 8, 2000, 8, 64, W.BF16, 2.5)
@@ -293,17 +281,16 @@ def test_plan_buffer_reuse_across_shapes(td, launch):
     ids_b, _ = W.make_routing(big, seed=4)
     ids_s, _ = W.make_routing(small, seed=4)
     lay = td.moonep_plan_layout(dims_s)
-    with plan_launch(launch):
-        run_plan(td, dims_b, ids_b, DEV, pb)
-        run_plan(td, dims_s, ids_s, DEV, pb[:lay.bytes])
+    run_plan(td, dims_b, ids_b, DEV, pb)
+    run_plan(td, dims_s, ids_s, DEV, pb[:lay.bytes])
     g = read_plan(td, dims_s, pb[:lay.bytes])
     assert_plan_equal(g, oracle.plan(small.R, small.E, small.K, small.S, small.B, ids_s))
 
 
-def test_fused_plan_from_arbitrary_buffer_contents(td):
-    """The one-launch plan's workgroups synchronise through words of the plan
-    buffer; any starting contents must work, and so must the values each call
-    leaves for the next."""
+@PLANS
+def test_plan_from_arbitrary_buffer_contents(td, bounded):
+    """The plan buffer needs no initialisation: any starting contents give the
+    same plan, and so do the values each call leaves for the next."""
     wl = _wl("sync", 8, 64, 8, 1500, 8, 64, W.BF16, 2.0)
     dims = _dims(td, wl)
     lay = td.moonep_plan_layout(dims)
@@ -318,53 +305,50 @@ def test_fused_plan_from_arbitrary_buffer_contents(td):
                                    dtype=torch.int32).to(torch.uint8))
         for seed in (0, 1, 2):
             ids, _ = W.make_routing(wl, seed)
-            with plan_launch("fused"):
-                run_plan(td, dims, ids, DEV, pb)
-            assert_plan_equal(read_plan(td, dims, pb), oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids))
+            run_plan(td, dims, ids, DEV, pb, bounded=bounded)
+            assert_plan_equal(read_plan(td, dims, pb),
+                              oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded))
 
 
-def test_fused_plan_graph_replays(td):
-    """A captured one-launch plan replayed on new ids: every replay reads the
-    generation afresh, so each one waits for its own tiles."""
+@PLANS
+def test_plan_graph_replays(td, bounded):
+    """The plan captured in a HIP graph and replayed on new ids: every replay
+    gives the oracle's plan for the ids it sees."""
     wl = _wl("graph", 8, 64, 8, 1000, 8, 64, W.BF16, 2.0)
     dims = _dims(td, wl)
     pb = td.new_plan_buffer(dims, DEV)
     ids0, _ = W.make_routing(wl, 0)
     ids_d = torch.from_numpy(ids0).to(DEV)
     s = torch.cuda.Stream(DEV)
-    with plan_launch("fused"):
-        with torch.cuda.stream(s):
-            td.moonep_plan(dims, ids_d, pb, stream=s)  # sets kernel attributes before capture
-        s.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=s):
-            td.moonep_plan(dims, ids_d, pb, stream=s)
+    plan_fn = td.moonep_plan_bounded if bounded else td.moonep_plan
+    with torch.cuda.stream(s):
+        plan_fn(dims, ids_d, pb, stream=s)  # sets kernel attributes before capture
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        plan_fn(dims, ids_d, pb, stream=s)
     for seed in (1, 2, 3, 1):
         ids, _ = W.make_routing(wl, seed)
         ids_d.copy_(torch.from_numpy(ids).to(DEV))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        assert_plan_equal(read_plan(td, dims, pb), oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids))
+        assert_plan_equal(read_plan(td, dims, pb),
+                          oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded))
 
 
 # ------------------------------------------------------------ full-size shapes
 
-# tiny, uniform and decode have at most 64 tiles: the water-fill in both forms
-@pytest.mark.parametrize("name,bounded,launch", [
-    ("tiny", False, "fused"), ("tiny", False, "multi"), ("tiny", True, None),
-    ("uniform", False, "fused"), ("uniform", False, "multi"), ("uniform", True, None),
-    ("zipf", False, None), ("zipf", True, None), ("k3", False, None), ("k3", True, None),
-    ("decode", False, "fused"), ("decode", False, "multi"), ("decode", True, None)])
-def test_workload_plans_all_seeds(td, name, bounded, launch):
+@PLANS
+@pytest.mark.parametrize("name", ["tiny", "uniform", "zipf", "k3", "decode"])
+def test_workload_plans_all_seeds(td, name, bounded):
     wl = W.WORKLOADS[name]
     dims = _dims(td, wl)
     pb = td.new_plan_buffer(dims, DEV)
     for seed in (0, 1, 2):
-        say(f"plan {name} seed {seed} bounded={bounded} launch={launch}")
+        say(f"plan {name} seed {seed} bounded={bounded}")
         ids, _ = W.make_routing(wl, seed)
-        with plan_launch(launch):
-            run_plan(td, dims, ids, DEV, pb, bounded=bounded)
+        run_plan(td, dims, ids, DEV, pb, bounded=bounded)
         g = read_plan(td, dims, pb)
         p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
         assert_plan_equal(g, p)

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 F32 = 0
 BF16 = 1
-STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B, STATUS_SYNC_TIMEOUT = 1, 2, 4, 8
+STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 
 ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded", "moonep_dispatch",
                 "moonep_replicate",
@@ -51,8 +51,8 @@ _LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D
                    "Dpre", "dst", "src", "n_dup", "dup_expert", "dup_start", "dup_count",
                    "seg_ptr", "seg_expert", "n_list", "list_expert", "list_rank", "list_b",
                    "dup_ptr", "ws_tile_counts", "ws_tile_status", "ws_mat_pre", "ws_xlist",
-                   "ws_n_x", "ws_piece_js", "ws_kept", "ws_koff", "ws_upre", "ws_sync",
-                   "ws_pslot", "ws_pcnt")
+                   "ws_n_x", "ws_piece_js", "ws_kept", "ws_koff", "ws_upre", "ws_pslot",
+                   "ws_pcnt")
 
 
 class Layout(ctypes.Structure):

@@ -90,7 +90,6 @@ PlanPtrs resolve(const moonep_layout &l, void *base) {
     p.kept = at(l.ws_kept);
     p.koff = at(l.ws_koff);
     p.upre = at(l.ws_upre);
-    p.sync = reinterpret_cast<uint64_t *>(static_cast<char *>(base) + l.ws_sync);
     p.pslot = at(l.ws_pslot);
     p.pcnt = at(l.ws_pcnt);
     return p;
@@ -155,7 +154,6 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     l.ws_kept = take(4 * E);
     l.ws_koff = take(4 * E);
     l.ws_upre = take(4 * (R + 1));
-    l.ws_sync = take(8 * ((int64_t)l.n_tiles + 1));
     l.ws_pslot = take(4 * (int64_t)l.pcap);
     l.ws_pcnt = take(4 * (int64_t)l.pcap);
     l.bytes = off;

@@ -27,7 +27,6 @@ struct PlanPtrs {
     int32_t *tile_counts, *tile_status, *mat_pre, *xlist, *n_x, *piece_js;
     int32_t *kept, *koff;  // per expert: rows kept at home, their first row there
     int32_t *upre;         // [R+1] exclusive prefix over ranks of slots left empty
-    uint64_t *sync;        // [1 + n_tiles] generation and tile arrivals of the one-launch plan
     int32_t *pslot, *pcnt; // [pcap] per list entry: first slot of the piece, its rows
 };
 
@@ -45,9 +44,7 @@ struct PlanShape {
 PlanPtrs resolve(const moonep_layout &lay, void *base);
 
 // bounded: the plan that keeps at most B duplicates per rank where it can
-// (k_solve_bounded) instead of the water-fill (k_solve). Four launches; with
-// MOONEP_PLAN_LAUNCH=fused the water-fill runs as one (k_plan_fused) on shapes
-// of at most 64 tiles whose workgroups all fit on the device at once.
+// (k_solve_bounded) instead of the water-fill (k_solve).
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st);
 

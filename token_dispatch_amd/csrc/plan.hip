@@ -26,9 +26,6 @@
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
 // waves of this tile) + (earlier chunks of this wave) + (earlier lanes of the
 // same 64-entry chunk), each an integer count taken in entry order.
-#include <stdlib.h>
-#include <string.h>
-
 #include "internal.h"
 
 namespace moonep {
@@ -869,15 +866,13 @@ __device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, const 
     }
 }
 
-// The plan tables the placement needs, into LDS (no barrier). With TBASE,
-// tile_counts[tile] must already hold the exclusive prefix over earlier tiles;
-// without it, the caller fills t.tbase.
-template <bool TBASE>
+// The plan tables the placement needs, into LDS (no barrier); tile_counts[tile]
+// already holds the exclusive prefix over earlier tiles.
 __device__ __forceinline__ void load_tables(const PlanShape &sh, const PlanPtrs &p, int tile,
                                             const AsgTables &t) {
     const int tid = threadIdx.x, E = sh.E, R = sh.R;
     if (tid < E) {
-        if (TBASE) t.tbase[tid] = p.tile_counts[(int64_t)tile * E + tid];
+        t.tbase[tid] = p.tile_counts[(int64_t)tile * E + tid];
         t.kept[tid] = p.kept[tid];
         t.kslot[tid] = (tid / sh.G) * sh.SK + p.koff[tid];
         t.dup_ptr[tid] = p.dup_ptr[tid];
@@ -1045,7 +1040,7 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     // loads first, all in flight: this wave's ids, then the tables
     int idv[kChunks];
     load_ids(ids, t, idv);
-    load_tables<true>(sh, p, t.tile, tb);
+    load_tables(sh, p, t.tile, tb);
     zero_pos(sh, s_pos);
     __syncthreads();
     uint64_t same[kChunks];
@@ -1057,263 +1052,15 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     plan_tails(sh, p, tb.upre);
 }
 
-// ---------------------------------------------------------------- k_plan_fused
-// The whole water-fill plan in one launch, for problems whose tiles all fit on
-// the GPU at once (the host checks that before choosing this kernel). The
-// bounded plan always takes four launches: its solve inlined here would not fit
-// the 128 registers a lane of a 16-wave workgroup may hold. One 1024-thread
-// workgroup per tile:
-//   1. it loads its ids (kept in registers to the end) and publishes its expert
-//      histogram;
-//   2. workgroup 0 waits for every tile, sums T over the tiles, runs the solve,
-//      publishes the plan tables and only then takes its own per-wave counts,
-//      in-chunk matches (the ballots of pass 1) and status bits; the others take
-//      theirs while the plan is being made, then wait for it;
-//   3. every workgroup adds its status bits, sums its tile's base over the
-//      earlier tiles and places its own entries.
-// tile_counts keeps each tile's own counts here (no scan in place).
-// Synchronisation is through ws_sync: [0] a generation number, [1 + t] tile t's
-// arrival. Each call reads the generation g; a tile arrives by storing g + 1,
-// and workgroup 0 releases by storing g + 1 as the new generation. Values left
-// by earlier calls are at most g, so any starting contents work. Every wait is
-// bounded: on time-out MOONEP_STATUS_SYNC_TIMEOUT is raised and every wave
-// still exits.
-constexpr int kFusedMaxTiles = 64;
-constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
-constexpr uint32_t kSpinLimit = 1u << 21;
-
-__device__ __forceinline__ uint64_t load_acquire(const uint64_t *a) {
-    return __hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_release(uint64_t *a, uint64_t v) {
-    __hip_atomic_store(a, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Polling reads: coherent at device scope but without the cache invalidation of
-// an acquire (one acquire fence follows the wait instead).
-__device__ __forceinline__ uint64_t load_relaxed(const uint64_t *a) {
-    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Sum of counts[t][e] over tiles t in [0, n_tiles), n_tiles <= kFusedMaxTiles:
-// 32 independent loads in flight per round.
-__device__ __forceinline__ int sum_tiles(const int32_t *counts, int E, int e, int n_tiles) {
-    int sum = 0;
-    for (int t0 = 0; t0 < n_tiles; t0 += 32) {
-        int v[32];
-#pragma unroll
-        for (int u = 0; u < 32; ++u) v[u] = t0 + u < n_tiles ? counts[(int64_t)(t0 + u) * E + e] : 0;
-#pragma unroll
-        for (int u = 0; u < 32; ++u) sum += v[u];
-    }
-    return sum;
-}
-
-inline size_t fused_lds_bytes(const PlanShape &sh) {
-    const int solve = wf_lds(sh.E, sh.R, sh.pcap, nullptr, nullptr);
-    const int tables = asg_tables(sh.E, sh.R, sh.pcap, nullptr, nullptr);
-    const int region = max(max(solve, tables), sh.E + kTileEntries);  // histogram + ids
-    return sizeof(int32_t) * (size_t)(pos_ints(sh) + 4 + region);
-}
-
-// This tile's status bits: invalid ids, and ids repeated within a token (valid
-// ones only). When K divides 64 a token's K entries are K aligned lanes of one
-// chunk, and the ballot masks already say which of them hold the same id;
-// otherwise the tile's ids are compared in LDS (s_ids).
-__device__ __forceinline__ int tile_status_bits(const PlanShape &sh, const Tile &t,
-                                                const int (&idv)[kChunks],
-                                                const uint64_t (&same)[kChunks],
-                                                const int32_t *s_ids) {
-    const int w = threadIdx.x >> 6, lane = lane_id(), K = sh.K;
-    const bool aligned = (64 % K) == 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-    const uint64_t group = (K == 64 ? ~0ull : ((1ull << K) - 1ull)) << (lane - lane % K);
-    int st = 0;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        const int i = w * (kChunks * 64) + c * 64 + lane;
-        const int e = idv[c];
-        if (i < t.n) {
-            if (e < 0 || e >= sh.E) {
-                st |= MOONEP_STATUS_BAD_ID;
-            } else if (aligned) {
-                if (same[c] & group & below) st |= MOONEP_STATUS_REPEAT_ID;
-            } else {
-                const int k = i % K;
-                for (int k2 = 1; k2 <= k; ++k2)
-                    if (s_ids[i - k2] == e) st |= MOONEP_STATUS_REPEAT_ID;
-            }
-        }
-    }
-    return st;
-}
-
-__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void k_plan_fused(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p, uint64_t *sync) {
-    extern __shared__ int32_t smem[];
-    const int tid = threadIdx.x, E = sh.E;
-    uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);  // kept from the ballots to step 3
-    int32_t *s_misc = smem + pos_ints(sh);                 // [0] status bits, [1] time-out
-    int32_t *region = s_misc + 4;                          // histogram and ids, solve, tables
-    int32_t *s_ids = region + E;                           // the tile's ids (kTileEntries)
-    const Tile t = tile_of(sh, blockIdx.x);
-
-    // 1. this tile's expert counts, published as soon as they are known
-    __shared__ uint64_t s_gen;
-    if (tid == 0) {
-        s_gen = load_acquire(sync);
-        s_misc[0] = 0;
-        s_misc[1] = 0;
-    }
-    int idv[kChunks];
-    load_ids(ids, t, idv);
-    for (int e = tid; e < E; e += kAssignThreads) region[e] = 0;
-    __syncthreads();
-    {
-        const int w = tid >> 6, lane = lane_id();
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int i = w * (kChunks * 64) + c * 64 + lane;
-            if (i < t.n) {
-                s_ids[i] = idv[c];
-                if (idv[c] >= 0 && idv[c] < E) atomicAdd(&region[idv[c]], 1);
-            }
-        }
-    }
-    __syncthreads();
-    if (tid < E) p.tile_counts[(int64_t)t.tile * E + tid] = region[tid];
-    if (tid == 0) p.tile_status[t.tile] = 0;  // this tile's bits reach the status in step 3
-    const uint64_t g = s_gen;
-    __syncthreads();
-    if (tid == 0) store_release(&sync[1 + t.tile], g + 1);
-
-    // 2. the plan tables: workgroup 0 solves while the others take their per-wave
-    // counts, in-chunk matches and status bits, then wait for the plan
-    uint64_t same[kChunks];
-    if (t.tile == 0) {
-        int late = 0;
-        if (tid < sh.n_tiles) {
-            uint32_t spins = 0;
-            while (load_relaxed(&sync[1 + tid]) != g + 1) {
-                if (++spins >= kSpinLimit) {
-                    late = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        if (__syncthreads_or(late) && tid == 0) p.tile_status[0] = MOONEP_STATUS_SYNC_TIMEOUT;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        // T from the tiles' counts (each tile's own base is summed in step 3)
-        if (tid < E) p.T[tid] = sum_tiles(p.tile_counts, E, tid, sh.n_tiles);
-        __syncthreads();
-        solve_waterfill(sh, p, region);
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) store_release(sync, g + 1);
-        // this tile's own matches, after the release: the ids are read again so
-        // that nothing of them stays in registers across the solve
-        load_ids(ids, t, idv);
-        for (int i = tid; i < t.n; i += kAssignThreads) s_ids[i] = ids[t.a0 + i];
-        zero_pos(sh, s_pos);
-        __syncthreads();
-        count_waves(sh, idv, same, s_pos);
-        const int st = tile_status_bits(sh, t, idv, same, s_ids);
-        if (st) atomicOr(&s_misc[0], st);
-        __syncthreads();
-    } else {
-        zero_pos(sh, s_pos);
-        __syncthreads();
-        count_waves(sh, idv, same, s_pos);
-        {
-            const int st = tile_status_bits(sh, t, idv, same, s_ids);
-            if (st) atomicOr(&s_misc[0], st);
-        }
-        if (tid == 0) {
-            uint32_t spins = 0;
-            while (load_relaxed(sync) == g) {
-                if (++spins >= kSpinLimit) {
-                    s_misc[1] = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        __syncthreads();
-        if (s_misc[1]) {  // the plan never came: leave this tile's entries alone
-            if (tid == 0) atomicOr(p.status, MOONEP_STATUS_SYNC_TIMEOUT);
-            return;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-
-    // 3. place this tile's entries; the tile's base is the sum over earlier tiles
-    if (tid == 0 && s_misc[0]) atomicOr(p.status, s_misc[0]);
-    AsgTables tb;
-    asg_tables(sh.E, sh.R, sh.pcap, region, &tb);
-    load_tables<false>(sh, p, t.tile, tb);
-    if (tid < E) tb.tbase[tid] = sum_tiles(p.tile_counts, E, tid, t.tile);
-    running_positions(sh, s_pos);
-    __syncthreads();
-    place_entries(sh, p, t, idv, same, s_pos, tb);
-    plan_tails(sh, p, tb.upre);
-}
-
-}  // namespace
-
-namespace {
-
 hipError_t allow_lds(const void *kernel, size_t lds) {
     if (lds <= 65536) return hipSuccess;  // within the default dynamic LDS limit of a launch
     return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
-// Workgroups of the fused kernel the current device holds at once with lds bytes
-// of LDS each.
-int fused_resident(const void *kernel, size_t lds) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAssignThreads, lds) !=
-        hipSuccess)
-        return 0;
-    return cus * per_cu;
-}
-
-// MOONEP_PLAN_LAUNCH=fused asks for the water-fill's one-launch form (an error
-// where the shape cannot take it); otherwise four launches. At the decode shape
-// the two forms took the same time (29.6 against 30.4 us of kernel time): the
-// two hand-overs between workgroups cost what the three kernel boundaries do.
-// The bounded plan always takes four launches.
-enum class Launch { Auto, Multi, Fused };
-
-Launch launch_mode() {
-    const char *v = getenv("MOONEP_PLAN_LAUNCH");
-    if (v && strcmp(v, "multi") == 0) return Launch::Multi;
-    if (v && strcmp(v, "fused") == 0) return Launch::Fused;
-    return Launch::Auto;
 }
 
 }  // namespace
 
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st) {
-    const Launch mode = launch_mode();
-    if (!bounded && sh.n_tiles <= kFusedMaxTiles && mode == Launch::Fused) {
-        const void *kf = (const void *)k_plan_fused;
-        const size_t lds = fused_lds_bytes(sh);
-        // a shape whose LDS the device cannot give one workgroup is not eligible
-        if (lds <= kMaxLdsBytes && allow_lds(kf, lds) == hipSuccess &&
-            fused_resident(kf, lds) >= sh.n_tiles) {
-            hipLaunchKernelGGL(k_plan_fused, dim3(sh.n_tiles), dim3(kAssignThreads), lds, st, ids, sh,
-                               p, p.sync);
-            return hipGetLastError();
-        }
-    }
-    if (mode == Launch::Fused && !bounded) return hipErrorInvalidConfiguration;
     const dim3 tiles(sh.n_tiles);
 #define MOONEP_COUNT(KM)                                                                    \
     hipLaunchKernelGGL(k_count<KM>, tiles, dim3(kPlanThreads), 0, st, ids, sh, p.tile_counts, \
