@@ -63,6 +63,12 @@ SMALL = [
     _wl("r1024", 1024, 1024, 2, 4, 2, 8, W.BF16, 2.0),
     # fp32 rows and a larger fp32 weight block
     _wl("f32_wide", 4, 16, 2, 1000, 4, 1024, W.F32, 2.5, block=(3, 64, 64)),
+    # K that is not a power of two: tokens straddle 64-entry chunks, tiles hold
+    # 4096 // K whole tokens, and the count kernel takes scalar id loads
+    _wl("k3_r3", 3, 27, 3, 1001, 3, 16, W.BF16, 2.5),
+    _wl("k6", 4, 48, 6, 777, 4, 64, W.BF16, 2.0),
+    _wl("k12_f32", 8, 96, 12, 300, 6, 40, W.F32, 1.5),
+    _wl("k40", 2, 80, 40, 120, 8, 64, W.BF16, 1.0),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
     W.WORKLOADS["tiny"],
 ]
