@@ -12,15 +12,20 @@
 //             tile's expert histogram in LDS, written to tile_counts[tile][E].
 //   k_scan    one workgroup per 64 experts: exclusive scan of tile_counts down
 //             the tiles (in place) and the column totals T[e].
-//   k_solve   one workgroup: home offsets, home load, keep / overflow / deficit
-//             and their prefix sums, then the duplicates as the intersections of
-//             each expert's overflow interval with each rank's deficit interval
-//             (a merge of two sorted boundary lists), and all plan tables.
-//   k_assign  one 1024-thread workgroup per token tile: the stable position of
-//             every entry inside its expert (tile base + per-wave base + in-wave
-//             rank from bit-sliced ballots), then its slot -- a home slot, or an
-//             offset into the one duplicate piece of its expert that holds its
-//             overflow index -- and the inverse map.
+//   k_solve   one workgroup (the water-fill): home offsets, home load, keep /
+//             overflow / deficit and their prefix sums, then the duplicates as
+//             the intersections of each expert's overflow interval with each
+//             rank's deficit interval (a merge of two sorted boundary lists),
+//             and all plan tables.
+//   k_solve_bounded  one workgroup (at most B duplicates per rank where it can):
+//             the same head, then each overloaded rank's overflow from its
+//             largest experts and one wave placing the pieces rank by rank.
+//   k_assign  one 1024-thread workgroup per token tile, for either plan: the
+//             stable position of every entry inside its expert (tile base +
+//             per-wave base + in-wave rank from bit-sliced ballots), then its
+//             slot -- a home slot below kept[e], else an offset into the one
+//             piece of its expert that holds its overflow row -- and the
+//             inverse map.
 //
 // Why this is exact: entry a's position inside expert e is the number of
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
