@@ -114,7 +114,8 @@ typedef struct moonep_layout {
     int32_t dcap;          /* max(1, min(SK, E - G)): most duplicates one rank can hold */
     int32_t pcap;          /* E + R: room for the global duplicate list                 */
     int32_t n_tiles;       /* token tiles of the plan kernels                           */
-    int32_t tile_tokens;   /* tokens per tile                                           */
+    int32_t tile_tokens;   /* tokens per tile: 4096, 2048 or 1024 entries rounded down
+                              to whole tokens, the largest giving at least 256 tiles  */
     int64_t status, maxT, maxvio, T, hoff, L, keep, O, D, Opre, Dpre, dst, src;
     int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
     int64_t n_list, list_expert, list_rank, list_b, dup_ptr;

@@ -49,7 +49,10 @@ def test_layout(td, shape):
     G, SK = E // R, S * K
     assert lay.dcap == max(1, min(SK, E - G))
     assert lay.pcap == E + R
-    assert lay.tile_tokens == 4096 // K
+    # the largest tile of 4096, 2048 or 1024 entries that still gives 256 tiles
+    n_ent = R * S * K
+    tile = next((t for t in (4096, 2048, 1024) if n_ent // t >= 256), 1024)
+    assert lay.tile_tokens == tile // K
     assert lay.n_tiles == -(-(R * S) // lay.tile_tokens)
     sizes = {"status": 4, "maxT": 4, "maxvio": 8, "T": 4 * E, "hoff": 4 * E, "L": 4 * R,
              "keep": 4 * R, "O": 4 * R, "D": 4 * R, "Opre": 4 * (R + 1), "Dpre": 4 * (R + 1),

@@ -44,6 +44,7 @@ PlanShape shape_of(const moonep_dims *d, const moonep_layout &lay) {
     s.pcap = lay.pcap;
     s.n_tiles = lay.n_tiles;
     s.tile_tokens = lay.tile_tokens;
+    s.tile_chunks = (lay.tile_tokens * d->K + 1023) / 1024;
     int bits = 0;
     while ((1 << bits) < d->E) ++bits;
     s.id_bits = bits;
@@ -113,7 +114,11 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     if (dcap < 1) dcap = 1;
     l.dcap = (int32_t)dcap;
     l.pcap = (int32_t)(E + R);
-    l.tile_tokens = kTileEntries / d->K;
+    // the largest tile (4096, 2048 or 1024 entries) that still gives kTileTarget
+    // tiles, so that small problems spread over more of the device
+    int64_t tile_entries = kTileEntries;
+    while (tile_entries > kMinTileEntries && NE / tile_entries < kTileTarget) tile_entries /= 2;
+    l.tile_tokens = (int32_t)(tile_entries / d->K);
     l.n_tiles = (int32_t)((n_tok + l.tile_tokens - 1) / l.tile_tokens);
     int64_t off = 0;
     auto take = [&off](int64_t bytes) {

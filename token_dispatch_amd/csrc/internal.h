@@ -13,7 +13,9 @@ namespace moonep {
 constexpr int kMaxE = 1024;        // LDS histogram bins of the plan kernels
 constexpr int kMaxR = 1024;        // one rank per thread in the solve kernel
 constexpr int kMaxK = 64;          // one entry of a token per lane
-constexpr int kTileEntries = 4096; // entries per plan tile (rounded down to whole tokens)
+constexpr int kTileEntries = 4096; // most entries per plan tile (rounded down to whole tokens)
+constexpr int kMinTileEntries = 1024;  // fewest: one 64-entry chunk per wave of a 16-wave tile
+constexpr int kTileTarget = 256;   // tiles wanted to spread the plan over the device
 constexpr int kPlanThreads = 256;  // count / assign workgroup
 constexpr int kSolveThreads = 1024;
 
@@ -38,6 +40,7 @@ struct PlanShape {
     int32_t n_ent;        // R*S*K
     int32_t dcap, pcap;
     int32_t n_tiles, tile_tokens;
+    int32_t tile_chunks;  // 64-entry chunks per wave of an assign tile (1 .. 4)
     int32_t id_bits;      // bits needed to tell expert ids apart (ceil log2 E, >= 1)
 };
 

@@ -808,8 +808,9 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, P
 }
 
 // ---------------------------------------------------------------- assign
-// Wave w of the tile takes entries [w*256, w*256 + 256) as kChunks chunks of 64,
-// lane l holding entry w*256 + c*64 + l of chunk c. Both plans place entries the
+// A tile has tile_chunks (1 to kChunks) 64-entry chunks per wave: wave w takes
+// entries [w*n, w*n + n), n = tile_chunks*64, lane l holding entry w*n + c*64 + l
+// of chunk c. Both plans place entries the
 // same way: an entry's position among its expert's entries (token, then k order)
 // below kept[e] is a home row from koff[e] on; position kept[e] + jj is overflow
 // row jj of the expert, in the one piece whose range [jj0, jj0 + count) holds it.
@@ -861,13 +862,13 @@ __device__ __forceinline__ Tile tile_of(const PlanShape &sh, int tile) {
     return Tile{tile, min(sh.tile_tokens, sh.n_tok - tok0) * sh.K, (int64_t)tok0 * sh.K};
 }
 
-__device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, const Tile &t,
-                                         int (&idv)[kChunks]) {
+__device__ __forceinline__ void load_ids(const PlanShape &sh, const int32_t *__restrict__ ids,
+                                         const Tile &t, int (&idv)[kChunks]) {
     const int w = threadIdx.x >> 6, lane = lane_id();
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-        const int i = w * (kChunks * 64) + c * 64 + lane;
-        idv[c] = i < t.n ? ids[t.a0 + i] : -1;
+        const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
+        idv[c] = c < sh.tile_chunks && i < t.n ? ids[t.a0 + i] : -1;
     }
 }
 
@@ -910,6 +911,7 @@ __device__ __forceinline__ void count_waves(const PlanShape &sh, const int (&idv
     const int half = (w & 1) * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
+        if (c >= sh.tile_chunks) break;
         const int e = idv[c];
         const bool valid = e >= 0 && e < sh.E;
         uint64_t mask = __ballot(valid);
@@ -953,8 +955,9 @@ __device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtr
     const int half = (w & 1) * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
+        if (c >= sh.tile_chunks) break;
         const int e = idv[c];
-        const int i = w * (kChunks * 64) + c * 64 + lane;
+        const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
         const bool valid = e >= 0 && e < sh.E;
         if (valid) {
             const uint64_t mask = same[c];
@@ -1044,7 +1047,7 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
 
     // loads first, all in flight: this wave's ids, then the tables
     int idv[kChunks];
-    load_ids(ids, t, idv);
+    load_ids(sh, ids, t, idv);
     load_tables(sh, p, t.tile, tb);
     zero_pos(sh, s_pos);
     __syncthreads();
