@@ -203,14 +203,24 @@ constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void k_scan(PlanShape sh,
                                                        int32_t *__restrict__ tile_counts,
                                                        int32_t *__restrict__ T) {
+    constexpr int kCache = 32;  // a wave's run of tiles kept in registers between the passes
     __shared__ int32_t s_part[kScanThreads / 64][64];
     const int lane = lane_id(), w = threadIdx.x >> 6;
     const int e = blockIdx.x * 64 + lane;
     const int nw = kScanThreads / 64;
     const int run = (sh.n_tiles + nw - 1) / nw;
     const int t0 = min(w * run, sh.n_tiles), t1 = min(t0 + run, sh.n_tiles);
+    const bool cached = t1 - t0 <= kCache;  // the same for every lane of the wave
+    int v[kCache];
     int sum = 0;
-    if (e < sh.E) {
+    if (cached) {
+        // all of the run's loads in flight at once
+#pragma unroll
+        for (int u = 0; u < kCache; ++u)
+            v[u] = (e < sh.E && t0 + u < t1) ? tile_counts[(int64_t)(t0 + u) * sh.E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kCache; ++u) sum += v[u];
+    } else if (e < sh.E) {
 #pragma unroll 8
         for (int t = t0; t < t1; ++t) sum += tile_counts[(int64_t)t * sh.E + e];
     }
@@ -218,18 +228,26 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(PlanShape sh,
     __syncthreads();
     int prefix = 0, total = 0;
     for (int i = 0; i < nw; ++i) {
-        const int v = s_part[i][lane];
-        prefix += i < w ? v : 0;
-        total += v;
+        const int x = s_part[i][lane];
+        prefix += i < w ? x : 0;
+        total += x;
     }
     if (e < sh.E) {
         int running = prefix;
+        if (cached) {
+#pragma unroll
+            for (int u = 0; u < kCache; ++u) {
+                if (t0 + u < t1) tile_counts[(int64_t)(t0 + u) * sh.E + e] = running;
+                running += v[u];
+            }
+        } else {
 #pragma unroll 8
-        for (int t = t0; t < t1; ++t) {
-            int32_t *c = tile_counts + (int64_t)t * sh.E + e;
-            const int v = *c;
-            *c = running;
-            running += v;
+            for (int t = t0; t < t1; ++t) {
+                int32_t *c = tile_counts + (int64_t)t * sh.E + e;
+                const int x = *c;
+                *c = running;
+                running += x;
+            }
         }
         if (w == 0) T[e] = total;
     }
