@@ -76,7 +76,7 @@ def test_layout(td, shape):
 @pytest.mark.parametrize("bad", [
     dict(R=0), dict(R=1025, E=2050), dict(E=900), dict(E=1025 * 1), dict(K=0), dict(K=65, E=896),
     dict(K=897), dict(S=0), dict(B=-1), dict(dtype=2), dict(H=0), dict(H=7), dict(dtype=0, H=6),
-    dict(R=32, S=1 << 23),
+    dict(R=32, S=1 << 23), dict(dtype=0, H=(1 << 31) - 1),
 ])
 def test_invalid_dims_rejected(td, bad):
     kw = dict(R=32, E=896, K=16, S=4096, B=28, dtype=1, H=7168)

@@ -23,9 +23,10 @@ int check_dims(const moonep_dims *d) {
     if (d->S < 1 || d->B < 0) return MOONEP_ERR_DIMS;
     if ((int64_t)d->R * d->S * d->K >= ((int64_t)1 << 31)) return MOONEP_ERR_DIMS;
     if (d->dtype != MOONEP_F32 && d->dtype != MOONEP_BF16) return MOONEP_ERR_DIMS;
-    if (d->H < 1 || (d->H * elem_bytes(d->dtype)) % 16 != 0) return MOONEP_ERR_DIMS;
+    const int64_t row = (int64_t)d->H * elem_bytes(d->dtype);
+    if (d->H < 1 || row % 16 != 0) return MOONEP_ERR_DIMS;
     // 16-byte chunks of one row are indexed with int32 inside the kernels
-    if (d->H * elem_bytes(d->dtype) / 16 >= ((int64_t)1 << 31)) return MOONEP_ERR_DIMS;
+    if (row / 16 >= ((int64_t)1 << 31)) return MOONEP_ERR_DIMS;
     return MOONEP_OK;
 }
 
@@ -252,7 +253,7 @@ int moonep_combine_backward(const moonep_dims *d, const void *plan_buf, const vo
     if (rc != MOONEP_OK) return rc;
     if (gout_dtype != MOONEP_F32 && gout_dtype != MOONEP_BF16) return MOONEP_ERR_DIMS;
     // grad_out rows must also split into 16-byte chunks
-    if ((d->H * elem_bytes(gout_dtype)) % 16 != 0) return MOONEP_ERR_DIMS;
+    if (((int64_t)d->H * elem_bytes(gout_dtype)) % 16 != 0) return MOONEP_ERR_DIMS;
     if (grad_y == nullptr && grad_w == nullptr) return MOONEP_OK;  // nothing asked for
     if (!aligned16(plan_buf) || !aligned16(grad_out)) return MOONEP_ERR_PTR;
     if (grad_y != nullptr && (!aligned16(grad_y) || !aligned16(topk_w))) return MOONEP_ERR_PTR;
