@@ -273,17 +273,17 @@ hipError_t launch_dispatch(const PlanShape &sh, const PlanPtrs &p, const void *h
     }
 }
 
-// Output bytes one combine launch writes (about): large enough that launch gaps
-// stay small, small enough that the chunk's stores come as one burst.
-constexpr int64_t kCombineChunkOutBytes = 56ll << 20;
-
+// One combine launch is one resident round: as many items as the device holds
+// waves of k_combine at once, one item per wave. Each launch's stores then come
+// at the end of its reads, and the next launch's reads start after them. At K3
+// that is 2048 tokens (28 MiB of output); a launch of 2048 tokens took the call
+// from 5.17 ms (4096) to 5.08 ms, and half a round under-fills the device.
 template <int CPL, bool IB, bool OB, bool UW>
 hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void *out,
                           int64_t n_tok, int32_t segs, int32_t C, int32_t K, int64_t n_slots,
-                          int64_t out_row_bytes, hipStream_t st) {
-    int64_t tok_per = kCombineChunkOutBytes / out_row_bytes;
-    if (tok_per < 64) tok_per = 64;
-    const int64_t per_launch = tok_per * segs;
+                          hipStream_t st) {
+    static int cache[64];
+    const int64_t per_launch = (int64_t)resident_wgs(k_combine<CPL, IB, OB, UW>, cache) * kMoveWaves;
     const int64_t items = n_tok * segs;
     for (int64_t lo = 0; lo < items; lo += per_launch) {
         const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
@@ -302,12 +302,11 @@ static hipError_t combine_typed(const PlanShape &sh, const PlanPtrs &p, const vo
     const int cpl = pick_cpl(C);
     const int32_t segs = (int32_t)((C + 64 * cpl - 1) / (64 * cpl));
     const int64_t n_slots = (int64_t)sh.n_ent;
-    const int64_t orow = H * (OB ? 2 : 4);
     auto yy = static_cast<const v4u *>(y);
 #define MOONEP_COMBINE(W)                                                                  \
     case W:                                                                                \
         return combine_chunks<W, IB, OB, UW>(yy, w, p.dst, out, sh.n_tok, segs, (int32_t)C, sh.K, \
-                                         n_slots, orow, st);
+                                         n_slots, st);
     switch (cpl) {
         MOONEP_COMBINE(1)
         MOONEP_COMBINE(2)
