@@ -49,6 +49,7 @@ PlanShape shape_of(const moonep_dims *d, const moonep_layout &lay) {
     int bits = 0;
     while ((1 << bits) < d->E) ++bits;
     s.id_bits = bits;
+    s.inv_k = 1.0f / (float)d->K;
     return s;
 }
 

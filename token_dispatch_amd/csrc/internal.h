@@ -42,6 +42,7 @@ struct PlanShape {
     int32_t n_tiles, tile_tokens;
     int32_t tile_chunks;  // 64-entry chunks per wave of an assign tile (1 .. 4)
     int32_t id_bits;      // bits needed to tell expert ids apart (ceil log2 E, >= 1)
+    float inv_k;          // 1/K rounded to nearest: token of an in-tile entry index
 };
 
 PlanPtrs resolve(const moonep_layout &lay, void *base);

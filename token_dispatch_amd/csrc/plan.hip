@@ -22,15 +22,16 @@
 //             largest experts and one wave placing the pieces rank by rank.
 //   k_assign  one 1024-thread workgroup per token tile, for either plan: the
 //             stable position of every entry inside its expert (tile base +
-//             per-wave base + in-wave rank from bit-sliced ballots), then its
+//             per-wave base + in-wave rank from per-token LDS atomics, or
+//             bit-sliced ballots for small K and repeated ids), then its
 //             slot -- a home slot below kept[e], else an offset into the one
 //             piece of its expert that holds its overflow row -- and the
 //             inverse map.
 //
 // Why this is exact: entry a's position inside expert e is the number of
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
-// waves of this tile) + (earlier chunks of this wave) + (earlier lanes of the
-// same 64-entry chunk), each an integer count taken in entry order.
+// waves of this tile) + (earlier entries of this wave), each an integer count
+// taken in entry order.
 #include "internal.h"
 
 namespace moonep {
@@ -923,27 +924,59 @@ __device__ __forceinline__ void zero_pos(const PlanShape &sh, uint32_t *s_pos) {
 
 // Pass 1: which lanes of each chunk hold the same id (bit-sliced ballots); the
 // lowest lane of each group adds the group's size to the wave's count.
-__device__ __forceinline__ void count_waves(const PlanShape &sh, const int (&idv)[kChunks],
-                                            uint64_t (&same)[kChunks], uint32_t *s_pos) {
+// Stable rank of every entry among this wave's entries of the same expert
+// ((token, k) order), while the wave's per-expert totals build up in s_pos.
+//
+// By tokens (K >= 4 and no repeated ids): the K ids of one token are distinct,
+// so the lanes of one token can add to their counters in one LDS atomic without
+// two of them meeting on a counter, and the value each gets back is the number
+// of earlier entries of its expert in the wave. The wave issues its tokens in
+// order and LDS runs a wave's operations in issue order. The token of in-tile
+// entry i is floor((i + 0.5) / K), taken in binary32: for i < 4096 and K <= 64
+// the quotient lies at least 1/128 from an integer and the rounding error is
+// below 1e-3, so the floor is exact.
+//
+// By id bit slices (small K, where a chunk holds many tokens, or repeated ids,
+// where two lanes of one atomic could meet): one ballot per id bit finds the
+// lanes holding the same id; the lowest of them adds their number and hands
+// the count before them back to the others.
+__device__ __forceinline__ void rank_entries(const PlanShape &sh, const int (&idv)[kChunks],
+                                             bool by_tokens, int (&rank)[kChunks],
+                                             uint32_t *s_pos) {
     const int w = threadIdx.x >> 6, lane = lane_id();
     const int half = (w & 1) * 16;
+    uint32_t *ctr = s_pos + (w >> 1) * sh.E;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         if (c >= sh.tile_chunks) break;
         const int e = idv[c];
         const bool valid = e >= 0 && e < sh.E;
-        uint64_t mask = __ballot(valid);
+        uint32_t got = 0;
+        if (by_tokens) {
+            const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
+            const int tok = (int)(((float)i + 0.5f) * sh.inv_k);
+            const int tok0 = __builtin_amdgcn_readlane(tok, 0);
+            const int n_sub = __builtin_amdgcn_readlane(tok, 63) - tok0 + 1;
+            for (int j = 0; j < n_sub; ++j)
+                if (valid && tok - tok0 == j) got = atomicAdd(&ctr[e], 1u << half);
+            rank[c] = (int)((got >> half) & 0xffffu);
+        } else {
+            uint64_t mask = __ballot(valid);
 #pragma unroll
-        for (int bit = 0; bit < kMaxIdBits; ++bit) {
-            if (bit < sh.id_bits) {
-                const bool set = valid && ((e >> bit) & 1);
-                const uint64_t bb = __ballot(set);
-                mask &= set ? bb : ~bb;
+            for (int bit = 0; bit < kMaxIdBits; ++bit) {
+                if (bit < sh.id_bits) {
+                    const bool set = valid && ((e >> bit) & 1);
+                    const uint64_t bb = __ballot(set);
+                    mask &= set ? bb : ~bb;
+                }
             }
+            const int lead = __ffsll((unsigned long long)mask) - 1;
+            if (valid && lane == lead) got = atomicAdd(&ctr[e], (uint32_t)__popcll(mask) << half);
+            const uint32_t base = (uint32_t)__shfl((int)got, lead < 0 ? 0 : lead);
+            const int below = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+            rank[c] = (int)((base >> half) & 0xffffu) + below;
         }
-        same[c] = mask;
-        if (valid && lane == __ffsll((unsigned long long)mask) - 1)
-            atomicAdd(&s_pos[(w >> 1) * sh.E + e], (uint32_t)__popcll(mask) << half);
     }
 }
 
@@ -963,11 +996,11 @@ __device__ __forceinline__ int running_positions(const PlanShape &sh, uint32_t *
     return (int)run;
 }
 
-// Pass 2: chunks in order; position = wave's running position + lanes below with
-// the same id; then the slot, dst and src.
+// Pass 2: position = the expert's entries in earlier tiles + in earlier waves of
+// this tile + the entry's rank in its wave; then the slot, dst and src.
 __device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
                                               const int (&idv)[kChunks],
-                                              const uint64_t (&same)[kChunks], uint32_t *s_pos,
+                                              const int (&rank)[kChunks], const uint32_t *s_pos,
                                               const AsgTables &tb) {
     const int w = threadIdx.x >> 6, lane = lane_id();
     const int half = (w & 1) * 16;
@@ -978,15 +1011,8 @@ __device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtr
         const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
         const bool valid = e >= 0 && e < sh.E;
         if (valid) {
-            const uint64_t mask = same[c];
-            const int below = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
             const int rel = (int)((s_pos[(w >> 1) * sh.E + e] >> half) & 0xffffu);
-            const int pos = tb.tbase[e] + rel + below;
-            // the wave's read above is issued before this add (LDS keeps a wave's
-            // operations in order); the other wave of the word only adds to its half
-            if (lane == 63 - __clzll((long long)mask))
-                atomicAdd(&s_pos[(w >> 1) * sh.E + e], (uint32_t)__popcll(mask) << half);
+            const int pos = tb.tbase[e] + rel + rank[c];
             const int kept = tb.kept[e];
             int slot = -1;
             if (pos < kept) {
@@ -1067,14 +1093,16 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     int idv[kChunks];
     load_ids(sh, ids, t, idv);
     load_tables(sh, p, t.tile, tb);
+    // the solve has the final status: repeated ids take the bit-slice ranks
+    const bool by_tokens = sh.K >= 4 && !(p.status[0] & MOONEP_STATUS_REPEAT_ID);
     zero_pos(sh, s_pos);
     __syncthreads();
-    uint64_t same[kChunks];
-    count_waves(sh, idv, same, s_pos);
+    int rank[kChunks];
+    rank_entries(sh, idv, by_tokens, rank, s_pos);
     __syncthreads();
     running_positions(sh, s_pos);
     __syncthreads();
-    place_entries(sh, p, t, idv, same, s_pos, tb);
+    place_entries(sh, p, t, idv, rank, s_pos, tb);
     plan_tails(sh, p, tb.upre);
 }
 
