@@ -46,6 +46,8 @@ static_assert(kMaxE <= kAssignThreads && kMaxR <= kAssignThreads && kMaxE <= kSo
                   kMaxR <= kSolveThreads,
               "one expert or rank per thread (the E-th / R-th prefix entries come from thread 0)");
 static_assert((1 << kMaxIdBits) >= kMaxE, "ids fit the ballot bit slices");
+static_assert(kSolveThreads == kAssignThreads, "assign uses the solve's block scan");
+static_assert(kTileEntries <= (1 << 22), "an in-tile index and an id share a word");
 static_assert(kMaxE <= 1024 && (kMaxE & (kMaxE - 1)) == 0, "expert ids fit the 10-bit field of a packed placement key");
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
@@ -847,9 +849,13 @@ struct AsgTables {
     int32_t *pcnt;     // rows of each piece
     int32_t *pslot;    // first slot of each piece
     int32_t *upre;     // R + 1: exclusive prefix of empty slots per rank
+    int32_t *toff;     // first index of e in this tile's expert-ordered list
+    uint32_t *ord;     // the tile's valid entries in (expert, token, k) order: i << 10 | e
+    int32_t *scan_w;   // block scan scratch
 };
 
-__host__ __device__ inline int asg_tables(int E, int R, int pcap, int32_t *base, AsgTables *o) {
+__host__ __device__ inline int asg_tables(int E, int R, int pcap, int cap, int32_t *base,
+                                          AsgTables *o) {
     LdsCarve c{base, 0};
     AsgTables t;
     t.tbase = c.take(E);
@@ -860,14 +866,25 @@ __host__ __device__ inline int asg_tables(int E, int R, int pcap, int32_t *base,
     t.pcnt = c.take(pcap);
     t.pslot = c.take(pcap);
     t.upre = c.take(R + 1);
+    t.toff = c.take(E);
+    t.ord = reinterpret_cast<uint32_t *>(c.take(cap));
+    t.scan_w = c.take(kAssignWaves + 1);
     if (o) *o = t;
     return c.off;
 }
 
-__host__ __device__ inline int pos_ints(const PlanShape &sh) { return (kAssignWaves / 2) * sh.E; }
+// Entries a tile's lanes can hold (a tile has at most that many).
+__host__ __device__ inline int tile_cap(const PlanShape &sh) { return sh.tile_chunks * kAssignThreads; }
+
+// s_pos also holds the tile's slots by entry once the positions are spent.
+__host__ __device__ inline int pos_ints(const PlanShape &sh) {
+    const int counts = (kAssignWaves / 2) * sh.E;
+    return counts > tile_cap(sh) ? counts : tile_cap(sh);
+}
 
 inline size_t assign_lds_bytes(const PlanShape &sh) {
-    return sizeof(int32_t) * (size_t)(pos_ints(sh) + asg_tables(sh.E, sh.R, sh.pcap, nullptr, nullptr));
+    return sizeof(int32_t) *
+           (size_t)(pos_ints(sh) + asg_tables(sh.E, sh.R, sh.pcap, tile_cap(sh), nullptr, nullptr));
 }
 
 struct Tile {
@@ -922,9 +939,7 @@ __device__ __forceinline__ void zero_pos(const PlanShape &sh, uint32_t *s_pos) {
         if ((int)threadIdx.x < sh.E) s_pos[m * sh.E + threadIdx.x] = 0u;
 }
 
-// Pass 1: which lanes of each chunk hold the same id (bit-sliced ballots); the
-// lowest lane of each group adds the group's size to the wave's count.
-// Stable rank of every entry among this wave's entries of the same expert
+// Pass 1: the stable rank of every entry among its wave's entries of its expert
 // ((token, k) order), while the wave's per-expert totals build up in s_pos.
 //
 // By tokens (K >= 4 and no repeated ids): the K ids of one token are distinct,
@@ -996,10 +1011,10 @@ __device__ __forceinline__ int running_positions(const PlanShape &sh, uint32_t *
     return (int)run;
 }
 
-// Pass 2: position = the expert's entries in earlier tiles + in earlier waves of
-// this tile + the entry's rank in its wave; then the slot, dst and src.
-__device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
-                                              const int (&idv)[kChunks],
+// Pass 2: every valid entry goes into the tile's expert-ordered list, at its
+// expert's start in the tile + the expert's entries in earlier waves + its rank
+// in its wave.
+__device__ __forceinline__ void order_entries(const PlanShape &sh, const int (&idv)[kChunks],
                                               const int (&rank)[kChunks], const uint32_t *s_pos,
                                               const AsgTables &tb) {
     const int w = threadIdx.x >> 6, lane = lane_id();
@@ -1008,37 +1023,58 @@ __device__ __forceinline__ void place_entries(const PlanShape &sh, const PlanPtr
     for (int c = 0; c < kChunks; ++c) {
         if (c >= sh.tile_chunks) break;
         const int e = idv[c];
-        const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
-        const bool valid = e >= 0 && e < sh.E;
-        if (valid) {
+        if (e >= 0 && e < sh.E) {
+            const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
             const int rel = (int)((s_pos[(w >> 1) * sh.E + e] >> half) & 0xffffu);
-            const int pos = tb.tbase[e] + rel + rank[c];
-            const int kept = tb.kept[e];
-            int slot = -1;
-            if (pos < kept) {
-                slot = tb.kslot[e] + pos;
-            } else {
-                const int jj = pos - kept;
-                const int q1 = tb.dup_ptr[e + 1];
-                for (int q = tb.dup_ptr[e]; q < q1; ++q) {
-                    const int d = jj - tb.pjj[q];
-                    if ((unsigned)d < (unsigned)tb.pcnt[q]) {
-                        slot = tb.pslot[q] + d;
-                        break;
-                    }
+            tb.ord[tb.toff[e] + rel + rank[c]] = ((uint32_t)i << 10) | (uint32_t)e;
+        }
+    }
+}
+
+// Pass 3, over the list: consecutive threads take consecutive entries of one
+// expert, whose slots are consecutive too, so the stores into the inverse map
+// come in runs instead of one cache line per lane. An entry's position p in its
+// expert is a home row below kept[e]; above, overflow row p - kept[e] lies in
+// exactly one piece of the expert. The slot of entry i also goes to s_dst[i].
+__device__ __forceinline__ void place_sorted(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
+                                             int n_valid, const AsgTables &tb, int32_t *s_dst) {
+    for (int j = threadIdx.x; j < n_valid; j += kAssignThreads) {
+        const uint32_t v = tb.ord[j];
+        const int i = (int)(v >> 10), e = (int)(v & 1023u);
+        const int pos = tb.tbase[e] + (j - tb.toff[e]);
+        const int kept = tb.kept[e];
+        int slot = -1;
+        if (pos < kept) {
+            slot = tb.kslot[e] + pos;
+        } else {
+            const int jj = pos - kept;
+            const int q1 = tb.dup_ptr[e + 1];
+            for (int q = tb.dup_ptr[e]; q < q1; ++q) {
+                const int d = jj - tb.pjj[q];
+                if ((unsigned)d < (unsigned)tb.pcnt[q]) {
+                    slot = tb.pslot[q] + d;
+                    break;
                 }
             }
-            // A correct plan always lands inside the buffer; the guard only keeps a
-            // broken invariant from turning into a wild store.
-            if ((unsigned)slot < (unsigned)sh.n_ent) {
-                p.dst[t.a0 + i] = slot;
-                p.src[slot] = (int32_t)(t.a0 + i);
-            } else {
-                p.dst[t.a0 + i] = -1;
-            }
-        } else if (i < t.n) {
-            p.dst[t.a0 + i] = -1;
         }
+        // A correct plan always lands inside the buffer; the guard only keeps a
+        // broken invariant from turning into a wild store.
+        if ((unsigned)slot < (unsigned)sh.n_ent) p.src[slot] = (int32_t)(t.a0 + i);
+        else slot = -1;
+        s_dst[i] = slot;
+    }
+}
+
+// Pass 4: dst in entry order, whole 64-entry runs per store; -1 for bad ids.
+__device__ __forceinline__ void write_dst(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
+                                          const int (&idv)[kChunks], const int32_t *s_dst) {
+    const int w = threadIdx.x >> 6, lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        if (c >= sh.tile_chunks) break;
+        const int i = w * (sh.tile_chunks * 64) + c * 64 + lane;
+        const int e = idv[c];
+        if (i < t.n) p.dst[t.a0 + i] = (e >= 0 && e < sh.E) ? s_dst[i] : -1;
     }
 }
 
@@ -1086,7 +1122,7 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
     uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
     AsgTables tb;
-    asg_tables(sh.E, sh.R, sh.pcap, smem + pos_ints(sh), &tb);
+    asg_tables(sh.E, sh.R, sh.pcap, tile_cap(sh), smem + pos_ints(sh), &tb);
     const Tile t = tile_of(sh, blockIdx.x);
 
     // loads first, all in flight: this wave's ids, then the tables
@@ -1100,9 +1136,18 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     int rank[kChunks];
     rank_entries(sh, idv, by_tokens, rank, s_pos);
     __syncthreads();
-    running_positions(sh, s_pos);
+    // the tile's count of expert threadIdx.x -> where the expert starts in the list
+    const int cnt = running_positions(sh, s_pos);
+    int start, n_valid;
+    block_excl_scan<1>(&cnt, &start, &n_valid, tb.scan_w);  // its barriers publish s_pos
+    if ((int)threadIdx.x < sh.E) tb.toff[threadIdx.x] = start;
     __syncthreads();
-    place_entries(sh, p, t, idv, rank, s_pos, tb);
+    order_entries(sh, idv, rank, s_pos, tb);
+    __syncthreads();
+    int32_t *s_dst = reinterpret_cast<int32_t *>(s_pos);  // the counts are spent
+    place_sorted(sh, p, t, n_valid, tb, s_dst);
+    __syncthreads();
+    write_dst(sh, p, t, idv, s_dst);
     plan_tails(sh, p, tb.upre);
 }
 
