@@ -127,6 +127,14 @@ __device__ __forceinline__ int lower_bound(const int *a, int n, int x) {
 // ---------------------------------------------------------------- k_count
 // KMAX: a power of two >= K; TPT tokens per thread cover the largest tile any K
 // in (KMAX/2, KMAX] gives. All of a thread's ids are loaded before any is used.
+// Repeated ids: each thread keeps a set of 1024 bits in LDS for its current
+// token (rows of 36 words: 16-byte aligned, and lanes 1 row apart start 4 banks
+// apart). Bit e is set with an atomic OR that returns the word's old value, so
+// a token's K ids cost K atomics instead of K(K-1)/2 compares; the atomics of
+// one lane run in program order, so a second e sees the first one's bit.
+constexpr int kSeenWords = kMaxE / 32;
+constexpr int kSeenStride = kSeenWords + 4;
+static_assert(kMaxE % 128 == 0, "a seen-set row is whole 16-byte groups");
 constexpr int tpt_of(int kmax) {
     return (kTileEntries / (kmax == 1 ? 1 : kmax / 2 + 1) + kPlanThreads - 1) / kPlanThreads;
 }
@@ -139,12 +147,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(const int32_t *__restric
     constexpr int TPT = tpt_of(KMAX);
     __shared__ int32_t s_hist[kMaxE];
     __shared__ int32_t s_st;
+    __shared__ __align__(16) uint32_t s_seen[kPlanThreads * kSeenStride];
     const int tile = blockIdx.x, tid = threadIdx.x;
     const int K = sh.K;
     const int tok0 = tile * sh.tile_tokens;
     const int ntok = min(sh.tile_tokens, sh.n_tok - tok0);
     for (int e = tid; e < sh.E; e += kPlanThreads) s_hist[e] = 0;
     if (tid == 0) s_st = 0;
+    uint32_t *seen = s_seen + tid * kSeenStride;  // this thread's own row: no barrier needed
+    if (KMAX > 1) {
+#pragma unroll
+        for (int q = 0; q < kSeenWords; q += 4)
+            *reinterpret_cast<uint4 *>(seen + q) = make_uint4(0u, 0u, 0u, 0u);
+    }
 
     // 16-byte loads when a token's ids are whole 16-byte groups (ids is 16-byte aligned)
     const bool vec = KMAX >= 4 && (K & 3) == 0;
@@ -174,20 +189,31 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(const int32_t *__restric
     int st = 0;
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
+        if (j * kPlanThreads + (tid & ~63) >= ntok) break;  // no token left in this wave
         const bool tok_ok = tid + j * kPlanThreads < ntok;
+        // no branches between the atomics, so they all issue before the first
+        // returned value is waited for; an absent or bad id adds 0 to word 0
+        uint32_t got[KMAX], bitv[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             const int e = v[j][k];
-            if (tok_ok && k < K) {
-                if (e < 0 || e >= sh.E) {
-                    st |= MOONEP_STATUS_BAD_ID;
-                } else {
-                    bool rep = false;
+            const bool in = tok_ok && k < K;
+            const bool ok = in && e >= 0 && e < sh.E;
+            if (in && !ok) st |= MOONEP_STATUS_BAD_ID;
+            const int ee = ok ? e : 0;
+            bitv[k] = ok ? 1u << (e & 31) : 0u;
+            if (KMAX > 1) got[k] = atomicOr(&seen[ee >> 5], bitv[k]);
+            atomicAdd(&s_hist[ee], ok ? 1 : 0);
+        }
+        if (KMAX > 1) {
 #pragma unroll
-                    for (int k2 = 0; k2 < k; ++k2) rep |= v[j][k2] == e;
-                    if (rep) st |= MOONEP_STATUS_REPEAT_ID;
-                    atomicAdd(&s_hist[e], 1);
-                }
+            for (int k = 0; k < KMAX; ++k)
+                if (got[k] & bitv[k]) st |= MOONEP_STATUS_REPEAT_ID;
+            // clear the words this token touched, ready for the thread's next token
+            if (j + 1 < TPT) {
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k)
+                    if (bitv[k]) seen[v[j][k] >> 5] = 0u;
             }
         }
     }
