@@ -69,6 +69,8 @@ SMALL = [
     _wl("k6", 4, 48, 6, 777, 4, 64, W.BF16, 2.0),
     _wl("k12_f32", 8, 96, 12, 300, 6, 40, W.F32, 1.5),
     _wl("k40", 2, 80, 40, 120, 8, 64, W.BF16, 1.0),
+    # 2048-entry plan tiles (two 64-entry chunks per assign wave), ragged last tile
+    _wl("tiles_2048", 8, 64, 8, 8200, 8, 64, W.BF16, 2.0),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
     W.WORKLOADS["tiny"],
 ]
