@@ -934,28 +934,65 @@ __device__ __forceinline__ void load_ids(const PlanShape &sh, const int32_t *__r
     }
 }
 
-// The plan tables the placement needs, into LDS (no barrier); tile_counts[tile]
-// already holds the exclusive prefix over earlier tiles.
-__device__ __forceinline__ void load_tables(const PlanShape &sh, const PlanPtrs &p, int tile,
-                                            const AsgTables &t) {
+// The plan tables the placement needs, fetched into registers with every load
+// in flight at once, and written to LDS later (no barrier), so that their
+// latency passes while the ranks are taken. tile_counts[tile] already holds the
+// exclusive prefix over earlier tiles. The whole piece table is fetched, with
+// no dependent loads: only entries below the list length are ever looked up
+// (through dup_ptr).
+static_assert(kMaxE + kMaxR <= 2 * kAssignThreads, "two piece-table entries per thread");
+struct TableRegs {
+    int tbase, kept, koff, dup_ptr, upre;  // expert (rank) threadIdx.x
+    int dup_end, upre_end;                 // dup_ptr[E] and upre[R]
+    int pjj[2], pcnt[2], pslot[2];         // list entries threadIdx.x and + kAssignThreads
+};
+
+// Every thread issues every load (indices clamped into range), so that the
+// number of loads in flight is the same on every path and the ranks can start
+// as soon as the ids are in, with the table loads still outstanding.
+__device__ __forceinline__ TableRegs fetch_tables(const PlanShape &sh, const PlanPtrs &p, int tile) {
+    const int tid = threadIdx.x, E = sh.E, R = sh.R;
+    const int e = min(tid, E - 1), r = min(tid, R);
+    TableRegs g;
+    g.tbase = p.tile_counts[(int64_t)tile * E + e];
+    g.kept = p.kept[e];
+    g.koff = p.koff[e];
+    g.dup_ptr = p.dup_ptr[e];
+    g.upre = p.upre[r];
+    g.dup_end = p.dup_ptr[E];
+    g.upre_end = p.upre[R];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int q = min(tid + k * kAssignThreads, sh.pcap - 1);
+        g.pjj[k] = p.piece_js[q];
+        g.pcnt[k] = p.pcnt[q];
+        g.pslot[k] = p.pslot[q];
+    }
+    return g;
+}
+
+__device__ __forceinline__ void store_tables(const PlanShape &sh, const TableRegs &g,
+                                             const AsgTables &t) {
     const int tid = threadIdx.x, E = sh.E, R = sh.R;
     if (tid < E) {
-        t.tbase[tid] = p.tile_counts[(int64_t)tile * E + tid];
-        t.kept[tid] = p.kept[tid];
-        t.kslot[tid] = (tid / sh.G) * sh.SK + p.koff[tid];
-        t.dup_ptr[tid] = p.dup_ptr[tid];
+        t.tbase[tid] = g.tbase;
+        t.kept[tid] = g.kept;
+        t.kslot[tid] = (tid / sh.G) * sh.SK + g.koff;
+        t.dup_ptr[tid] = g.dup_ptr;
     }
-    if (tid < R) t.upre[tid] = p.upre[tid];
+    if (tid < R) t.upre[tid] = g.upre;
     if (tid == 0) {
-        t.dup_ptr[E] = p.dup_ptr[E];
-        t.upre[R] = p.upre[R];
+        t.dup_ptr[E] = g.dup_end;
+        t.upre[R] = g.upre_end;
     }
-    // the whole piece table, no dependent loads: only entries below the list
-    // length are ever looked up (through dup_ptr)
-    for (int q = tid; q < sh.pcap; q += kAssignThreads) {
-        t.pjj[q] = p.piece_js[q];
-        t.pcnt[q] = p.pcnt[q];
-        t.pslot[q] = p.pslot[q];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int q = tid + k * kAssignThreads;
+        if (q < sh.pcap) {
+            t.pjj[q] = g.pjj[k];
+            t.pcnt[q] = g.pcnt[k];
+            t.pslot[q] = g.pslot[k];
+        }
     }
 }
 
@@ -1151,16 +1188,18 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     asg_tables(sh.E, sh.R, sh.pcap, tile_cap(sh), smem + pos_ints(sh), &tb);
     const Tile t = tile_of(sh, blockIdx.x);
 
-    // loads first, all in flight: this wave's ids, then the tables
+    // loads first, all in flight: this wave's ids, then the tables, which are
+    // only needed once the ranks are taken
     int idv[kChunks];
     load_ids(sh, ids, t, idv);
-    load_tables(sh, p, t.tile, tb);
+    const TableRegs regs = fetch_tables(sh, p, t.tile);
     // the solve has the final status: repeated ids take the bit-slice ranks
     const bool by_tokens = sh.K >= 4 && !(p.status[0] & MOONEP_STATUS_REPEAT_ID);
     zero_pos(sh, s_pos);
     __syncthreads();
     int rank[kChunks];
     rank_entries(sh, idv, by_tokens, rank, s_pos);
+    store_tables(sh, regs, tb);
     __syncthreads();
     // the tile's count of expert threadIdx.x -> where the expert starts in the list
     const int cnt = running_positions(sh, s_pos);
