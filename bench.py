@@ -159,6 +159,20 @@ def plan_latency(plan_fn, dims, ids_d, plan_buf, stream, iters):
     return out
 
 
+def host_cpu() -> str:
+    """The host's CPU model and logical CPU count, as the baseline's context."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
 def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
     """The oracle as it stands, single thread, on a bounded sample of the workload:
     the full plan; dispatch of whole destination-rank windows (the oracle streams
@@ -210,6 +224,7 @@ def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
                    f"scaled x{wl.n_tok / n:.1f})"),
         "plan_us": round(t_plan * 1e6, 1),
         "measured_s": round(t_plan + t_disp + t_comb, 2),
+        "host": host_cpu(),
     }
 
 
