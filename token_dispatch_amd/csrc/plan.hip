@@ -365,8 +365,8 @@ struct LdsCarve {
 constexpr int kScanScratch = (kSolveThreads / 64 + 1) * 4;  // block_excl_scan<NV <= 4>
 
 struct WfLds {
-    int32_t *T, *cum, *ovpre, *nzpre, *ovlist, *listE;
-    int32_t *keep, *O, *D, *Dpre, *dbeg, *dend, *nzlo, *ppre, *w, *scal;
+    int32_t *T, *cum, *ovpre, *ovp, *ovlist, *listE;
+    int32_t *keep, *O, *D, *Dpre, *dbeg, *dend, *nzlo, *rnp, *ppre, *w, *scal;
 };
 
 __host__ __device__ inline int wf_lds(int E, int R, int pcap, int32_t *base, WfLds *o) {
@@ -375,7 +375,7 @@ __host__ __device__ inline int wf_lds(int E, int R, int pcap, int32_t *base, WfL
     l.T = c.take(E);
     l.cum = c.take(E + 1);     // exclusive prefix of T over all experts
     l.ovpre = c.take(E + 1);   // exclusive prefix of each expert's overflow
-    l.nzpre = c.take(E + 1);   // exclusive prefix of (overflow > 0)
+    l.ovp = c.take(E + 1);     // overflow starts of the experts with overflow, then the total
     l.ovlist = c.take(E);      // experts with overflow, ascending
     l.listE = c.take(pcap);
     l.keep = c.take(R);
@@ -385,6 +385,7 @@ __host__ __device__ inline int wf_lds(int E, int R, int pcap, int32_t *base, WfL
     l.dbeg = c.take(R);
     l.dend = c.take(R);
     l.nzlo = c.take(R);
+    l.rnp = c.take(R);         // pieces per rank
     l.ppre = c.take(R + 1);
     l.w = c.take(kScanScratch);
     l.scal = c.take(4);        // status, maxT
@@ -440,10 +441,10 @@ inline size_t solve_lds_bytes(const PlanShape &sh, bool bounded) {
 __device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t *smem) {
     WfLds L;
     wf_lds(sh.E, sh.R, sh.pcap, smem, &L);
-    int *const s_T = L.T, *const s_cum = L.cum, *const s_ovpre = L.ovpre, *const s_nzpre = L.nzpre;
+    int *const s_T = L.T, *const s_cum = L.cum, *const s_ovpre = L.ovpre, *const s_ovp = L.ovp;
     int *const s_ovlist = L.ovlist, *const s_listE = L.listE, *const s_keep = L.keep, *const s_O = L.O;
     int *const s_D = L.D, *const s_Dpre = L.Dpre, *const s_dbeg = L.dbeg, *const s_dend = L.dend;
-    int *const s_nzlo = L.nzlo, *const s_ppre = L.ppre, *const s_w = L.w;
+    int *const s_nzlo = L.nzlo, *const s_rnp = L.rnp, *const s_ppre = L.ppre, *const s_w = L.w;
     int &s_status = L.scal[0], &s_maxT = L.scal[1];
 
     const int tid = threadIdx.x;
@@ -470,31 +471,44 @@ __device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t 
     }
     if (tid < E) {
         s_ovpre[tid] = pre[2];
-        s_nzpre[tid] = pre[3];
-        if (ov > 0) s_ovlist[pre[3]] = tid;
+        if (ov > 0) {
+            s_ovlist[pre[3]] = tid;
+            s_ovp[pre[3]] = pre[2];
+        }
     }
     if (tid == 0) {
         p.Opre[R] = totO;
         p.Dpre[R] = totD;
         s_Dpre[R] = totD;
         s_ovpre[E] = tot[2];
-        s_nzpre[E] = totNZ;
+        s_ovp[totNZ] = tot[2];
     }
     __syncthreads();
 
-    // pieces per deficit rank: overflowing experts whose interval meets the
-    // rank's filled deficit interval [dbeg, dend)
+    // pieces per deficit rank: the overflowing experts whose interval meets the
+    // rank's filled deficit interval [dbeg, dend), found in the compact list of
+    // overflow starts. Threads 2r and 2r + 1 search for the two ends at once;
+    // every lane runs the same iterations, so the pair exchange sees both.
+    for (int x0 = 0; x0 < 2 * R; x0 += kSolveThreads) {
+        const int x = x0 + tid, r = x >> 1;
+        int dbeg = 0, dend = 0, k = 0;
+        if (r < R) {
+            dbeg = min(s_Dpre[r], totO);
+            dend = min(s_Dpre[r + 1], totO);
+            if (dend > dbeg) k = upper_bound(s_ovp, totNZ + 1, (x & 1) ? dend - 1 : dbeg) - 1;
+        }
+        const int k_end = __shfl_xor(k, 1);
+        if (r < R && (x & 1) == 0) {
+            s_dbeg[r] = dbeg;
+            s_dend[r] = dend;
+            s_nzlo[r] = k;
+            s_rnp[r] = dend > dbeg ? k_end - k + 1 : 0;
+        }
+    }
+    __syncthreads();
     int np = 0;
     if (tid < R) {
-        const int dbeg = min(s_Dpre[tid], totO), dend = min(s_Dpre[tid + 1], totO);
-        s_dbeg[tid] = dbeg;
-        s_dend[tid] = dend;
-        if (dend > dbeg) {
-            const int elo = upper_bound(s_ovpre, E + 1, dbeg) - 1;
-            const int ehi = upper_bound(s_ovpre, E + 1, dend - 1) - 1;
-            np = s_nzpre[ehi + 1] - s_nzpre[elo];
-            s_nzlo[tid] = s_nzpre[elo];
-        }
+        np = s_rnp[tid];
         p.n_dup[tid] = np;
         if (np > sh.B) atomicOr(&s_status, MOONEP_STATUS_OVER_B);
     }
