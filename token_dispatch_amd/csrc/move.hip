@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kMoveThreads) void k_replicate(
 }
 
 // ---------------------------------------------------------------- reduce
+// Every byte is touched once per call, so loads and stores are non-temporal
+// (2.56 -> 2.45 ms at K3). Items of 8 vectors per thread were slower.
 constexpr int kRedUnroll = 4;
 constexpr int kRedVecs = kMoveThreads * kRedUnroll;  // float4 per work item
 
@@ -201,7 +203,10 @@ __global__ __launch_bounds__(kMoveThreads) void k_reduce(
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
             const int64_t j = j0 + (int64_t)i * kMoveThreads;
-            if (j < n4) acc[i] = h[j];
+            if (j < n4) {
+                const v4f hv = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(h) + j);
+                acc[i] = make_float4(hv.x, hv.y, hv.z, hv.w);
+            }
         }
         for (int q = p0; q < p1; ++q) {
             const int b = list_b[q], rk = list_rank[q];
@@ -211,7 +216,8 @@ __global__ __launch_bounds__(kMoveThreads) void k_reduce(
             for (int i = 0; i < kRedUnroll; ++i) {
                 const int64_t j = j0 + (int64_t)i * kMoveThreads;
                 if (j < n4) {
-                    const float4 t = g[j];
+                    const v4f tv = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(g) + j);
+                    const float4 t = make_float4(tv.x, tv.y, tv.z, tv.w);
                     acc[i].x = acc[i].x + t.x;
                     acc[i].y = acc[i].y + t.y;
                     acc[i].z = acc[i].z + t.z;
@@ -222,7 +228,9 @@ __global__ __launch_bounds__(kMoveThreads) void k_reduce(
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
             const int64_t j = j0 + (int64_t)i * kMoveThreads;
-            if (j < n4) h[j] = acc[i];
+            if (j < n4)
+                __builtin_nontemporal_store(v4f{acc[i].x, acc[i].y, acc[i].z, acc[i].w},
+                                            reinterpret_cast<v4f *>(h) + j);
         }
     }
 }
