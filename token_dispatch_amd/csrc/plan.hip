@@ -26,7 +26,8 @@
 //             bit-sliced ballots for small K and repeated ids), then its
 //             slot -- a home slot below kept[e], else an offset into the one
 //             piece of its expert that holds its overflow row -- and the
-//             inverse map.
+//             inverse map, walking the tile's entries in expert order so that
+//             the inverse-map stores come in runs of consecutive slots.
 //
 // Why this is exact: entry a's position inside expert e is the number of
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
