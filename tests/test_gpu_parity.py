@@ -229,6 +229,27 @@ def test_invalid_and_repeated_ids(td, bounded):
 
 
 @PLANS
+def test_repeated_ids_several_tokens_per_thread(td, bounded):
+    # K = 2 and 512 tokens per 1024-entry tile: counting thread t takes tokens
+    # t and t + 256 of its tile in turn, so its per-token seen set must be
+    # cleared between them. Token t + 256 names the ids of token t, swapped (no
+    # repeat); then a few tokens repeat one id, first and second tokens alike.
+    wl = _wl("rep_k2", 2, 16, 2, 2000, 2, 32, W.BF16, 1.0)
+    dims = _dims(td, wl)
+    assert td.moonep_plan_layout(dims).tile_tokens == 512
+    ids, w = W.make_routing(wl, seed=3)
+    ids = ids.reshape(-1, wl.K).copy()
+    for t0 in range(0, wl.n_tok, 512):
+        n2 = max(0, min(256, wl.n_tok - t0 - 256))
+        ids[t0 + 256:t0 + 256 + n2] = ids[t0:t0 + n2][:, ::-1]
+    g = _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
+    assert (int(g["status"][0]) & 2) == 0
+    ids[[5, 300, 512 + 40, 3000], 1] = ids[[5, 300, 512 + 40, 3000], 0]
+    g = _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 3, bounded)
+    assert int(g["status"][0]) & 2
+
+
+@PLANS
 def test_extreme_skew_and_balance(td, bounded):
     # every token picks the same K experts, all homed on rank 0
     wl = _wl("one_hot_rank", 8, 64, 8, 1000, 8, 64, W.BF16, 0.0)
