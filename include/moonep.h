@@ -280,6 +280,23 @@ int moonep_combine_backward(const moonep_dims *dims, const void *plan_buf, const
 int moonep_dispatch_backward(const moonep_dims *dims, const void *plan_buf, const void *grad_recv,
                              void *grad_hidden, int32_t out_dtype, void *stream);
 
+/*
+ * moonep_launch_count -- how many kernel launches one call of a chunked move
+ * enqueues on the current device, for profiling: per-launch durations that a
+ * kernel trace reports times this count give the call's time.
+ *
+ *   op          MOONEP_OP_DISPATCH (moonep_dispatch) or MOONEP_OP_COMBINE
+ *               (moonep_combine with out_dtype = dims->dtype)
+ *   n_launches  host, written on success
+ *
+ * Host only, launches nothing. The count depends on the dims and on how many
+ * workgroups of the move kernel the current device holds at once (read once per
+ * device). Returns MOONEP_OK, MOONEP_ERR_DIMS (bad dims or op) or
+ * MOONEP_ERR_PTR (n_launches == NULL).
+ */
+enum { MOONEP_OP_DISPATCH = 1, MOONEP_OP_COMBINE = 2 };
+int moonep_launch_count(const moonep_dims *dims, int32_t op, int32_t *n_launches);
+
 /* Text of a return value. Never NULL; the string is static. */
 const char *moonep_strerror(int rc);
 

@@ -111,6 +111,13 @@ def test_pointer_and_size_errors(td):
     d0 = _dims(td, B=0)
     assert lib.moonep_replicate(ctypes.byref(d0), None, None, None, 16, None) == 0
     assert lib.moonep_reduce_dup_grads(ctypes.byref(d0), None, None, None, 4, None) == 0
+    n = ctypes.c_int32(0)
+    assert lib.moonep_launch_count(ctypes.byref(d), td.OP_DISPATCH, None) == -2
+    assert lib.moonep_launch_count(None, td.OP_DISPATCH, ctypes.byref(n)) == -2
+    for op in (0, 3, -1):
+        assert lib.moonep_launch_count(ctypes.byref(d), op, ctypes.byref(n)) == -1
+    assert lib.moonep_launch_count(ctypes.byref(_dims(td, E=900)), td.OP_COMBINE,
+                                   ctypes.byref(n)) == -1
     for rc in (0, -1, -2, -3, -4, 5):
         assert td.moonep_strerror(rc)
 

@@ -281,6 +281,19 @@ def test_identity_expert_mean_returns_hidden(td):
     assert torch.equal(out.view(torch.int16), hid.view(torch.int16))
 
 
+def test_launch_count(td):
+    """The per-call launch count of the chunked moves: one launch for a small
+    problem, several at the K3 shape, and counting enqueues nothing."""
+    for name, several in (("tiny", False), ("k3", True)):
+        wl = W.WORKLOADS[name]
+        dims = _dims(td, wl)
+        for op in (td.OP_DISPATCH, td.OP_COMBINE):
+            n = td.moonep_launch_count(dims, op)
+            assert 1 <= n <= wl.n_tok
+            assert (n > 1) == several, (name, op, n)
+    torch.cuda.synchronize()
+
+
 def test_deterministic_and_stream_ordered(td):
     wl = W.WORKLOADS["zipf"].replace(S=512)
     dims = _dims(td, wl)

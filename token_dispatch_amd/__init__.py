@@ -28,11 +28,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 F32 = 0
 BF16 = 1
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
+OP_DISPATCH, OP_COMBINE = 1, 2
 
 ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded", "moonep_dispatch",
                 "moonep_replicate",
                 "moonep_combine", "moonep_reduce_dup_grads", "moonep_combine_backward",
-                "moonep_dispatch_backward", "moonep_strerror")
+                "moonep_dispatch_backward", "moonep_launch_count", "moonep_strerror")
 
 
 class Dims(ctypes.Structure):
@@ -72,6 +73,7 @@ _lib.moonep_combine.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp, _i32, _vp]
 _lib.moonep_reduce_dup_grads.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
 _lib.moonep_combine_backward.argtypes = [_P_DIMS, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.moonep_dispatch_backward.argtypes = [_P_DIMS, _vp, _vp, _vp, _i32, _vp]
+_lib.moonep_launch_count.argtypes = [_P_DIMS, _i32, ctypes.POINTER(ctypes.c_int32)]
 _lib.moonep_strerror.argtypes = [ctypes.c_int]
 _lib.moonep_strerror.restype = ctypes.c_char_p
 for _n in ENTRY_POINTS[:-1]:
@@ -129,6 +131,14 @@ def moonep_plan_layout(dims: Dims) -> Layout:
     lay = Layout()
     _check(_lib.moonep_plan_layout(ctypes.byref(dims), ctypes.byref(lay)), "moonep_plan_layout")
     return lay
+
+
+def moonep_launch_count(dims: Dims, op: int) -> int:
+    """Kernel launches one moonep_dispatch (OP_DISPATCH) or moonep_combine
+    (OP_COMBINE, output in dims.dtype) call enqueues on the current device."""
+    n = ctypes.c_int32(0)
+    _check(_lib.moonep_launch_count(ctypes.byref(dims), op, ctypes.byref(n)), "moonep_launch_count")
+    return int(n.value)
 
 
 def moonep_plan(dims: Dims, topk_ids, plan_buf, stream=None) -> None:

@@ -283,6 +283,28 @@ int moonep_dispatch_backward(const moonep_dims *d, const void *plan_buf, const v
                                               static_cast<hipStream_t>(stream)));
 }
 
+int moonep_launch_count(const moonep_dims *d, int32_t op, int32_t *n_launches) {
+    if (n_launches == nullptr) return MOONEP_ERR_PTR;
+    moonep_layout l;
+    const int rc = moonep_plan_layout(d, &l);
+    if (rc != MOONEP_OK) return rc;
+    if (op != MOONEP_OP_DISPATCH && op != MOONEP_OP_COMBINE) return MOONEP_ERR_DIMS;
+    const PlanShape sh = shape_of(d, l);
+    // the launchers only count while t_count_launches is set: no pointer is used
+    const PlanPtrs p{};
+    int32_t n = 0;
+    t_count_launches = &n;
+    const hipError_t e =
+        op == MOONEP_OP_DISPATCH
+            ? launch_dispatch(sh, p, nullptr, nullptr, d->H * elem_bytes(d->dtype), nullptr)
+            : launch_combine(sh, p, nullptr, nullptr, nullptr, d->dtype == MOONEP_BF16,
+                             d->dtype == MOONEP_BF16, d->H, nullptr);
+    t_count_launches = nullptr;
+    if (e != hipSuccess) return MOONEP_ERR_HIP;
+    *n_launches = n;
+    return MOONEP_OK;
+}
+
 const char *moonep_strerror(int rc) {
     switch (rc) {
         case MOONEP_OK: return "ok";

@@ -47,6 +47,10 @@ struct PlanShape {
 
 PlanPtrs resolve(const moonep_layout &lay, void *base);
 
+// While non-null on the calling thread, the chunked move launchers (dispatch,
+// combine) add their launches to it and enqueue nothing.
+extern thread_local int32_t *t_count_launches;
+
 // bounded: the plan that keeps at most B duplicates per rank where it can
 // (k_solve_bounded) instead of the water-fill (k_solve).
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,

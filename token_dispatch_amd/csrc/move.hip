@@ -240,6 +240,8 @@ constexpr int kCopyGrid = 256 * 8;
 
 }  // namespace
 
+thread_local int32_t *t_count_launches = nullptr;
+
 template <int CPL>
 hipError_t dispatch_chunks(const v4u *h, v4u *r, const int32_t *dst, int64_t items, int32_t segs,
                            int32_t C, int32_t K, int64_t n_slots, hipStream_t st) {
@@ -252,6 +254,10 @@ hipError_t dispatch_chunks(const v4u *h, v4u *r, const int32_t *dst, int64_t ite
         // the last launch only needs enough waves for what is left
         const int64_t waves = (hi - lo + TPW - 1) / TPW;
         const int64_t wgs = (waves + kMoveWaves - 1) / kMoveWaves;
+        if (t_count_launches != nullptr) {
+            ++*t_count_launches;
+            continue;
+        }
         hipLaunchKernelGGL((k_dispatch<CPL, TPW>), dim3((unsigned)(wgs < full ? wgs : full)),
                            dim3(kMoveThreads), 0, st, h, r, dst, lo, hi, segs, C, K, n_slots);
         const hipError_t e = hipGetLastError();
@@ -296,6 +302,10 @@ hipError_t combine_chunks(const v4u *y, const float *w, const int32_t *dst, void
     for (int64_t lo = 0; lo < items; lo += per_launch) {
         const int64_t hi = items - lo < per_launch ? items : lo + per_launch;
         const dim3 grid((unsigned)((hi - lo + kMoveWaves - 1) / kMoveWaves));
+        if (t_count_launches != nullptr) {
+            ++*t_count_launches;
+            continue;
+        }
         hipLaunchKernelGGL((k_combine<CPL, IB, OB, UW>), grid, dim3(kMoveThreads), 0, st, y, w, dst,
                            out, lo, hi, segs, C, K, n_slots);
         const hipError_t e = hipGetLastError();
