@@ -23,6 +23,8 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
             -- pinned: torch autograd in binary64 of the plain forward
                definitions (gather, weighted sum), torch's bf16 rounding, closed
                forms (unit weights, K copies of a bf16 row), binary64 error bounds
+tests/test_oracle_mutants.py plants mistakes in copies of the C source and checks
+that the pins above reject every one of them.
 """
 from __future__ import annotations
 
@@ -66,12 +68,21 @@ class _PlanOut(ctypes.Structure):
             "list_expert", "list_rank", "list_b", "dup_ptr")]
 
 
+# Test hook: the mutation test (tests/test_oracle_mutants.py) runs the pins in a
+# child process with this variable naming a deliberately broken build of the
+# oracle, to show that the pins reject it. Nothing else sets it.
+LIB_OVERRIDE_ENV = "MOONEP_ORACLE_LIB"
+
+
 def _load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get(LIB_OVERRIDE_ENV)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        lib = ctypes.CDLL(path)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_plan.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, _P(_PlanOut)]
         lib.oracle_plan.restype = ctypes.c_int

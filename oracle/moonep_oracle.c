@@ -138,8 +138,10 @@ int oracle_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
         } else {
             int64_t j = o->Opre[r] + (h - SK);
             d = find_deficit_rank(o->Dpre, R, j);
+            if (d < 0) { free(seen); return -1; }  /* Opre[R] != Dpre[R]: inconsistent */
             slot = o->keep[d] + (j - o->Dpre[d]);
         }
+        if (slot < 0 || slot >= SK) { free(seen); return -1; }
         o->dst[a] = (int32_t)(d * SK + slot);
         o->src[d * SK + slot] = (int32_t)a;
     }
@@ -546,7 +548,7 @@ int oracle_plan_bounded(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
                 if (pe[q] == e && pfirst[q] <= j && j < pfirst[q] + pcount[q])
                     slot = pr[q] * SK + pstart[q] + (j - pfirst[q]);
         }
-        if (slot < 0) goto out;
+        if (slot < 0 || slot >= NE) goto out;
         o->dst[a] = (int32_t)slot;
         o->src[slot] = (int32_t)a;
     }
