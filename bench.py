@@ -285,14 +285,16 @@ def main():
           file=sys.stderr, flush=True)
     ids, w = W.make_routing(wl, args.seed)
     dims = td.Dims(wl.R, wl.E, wl.K, wl.S, wl.B, wl.dtype, wl.H)
+    # model state first (expert weights, duplicate slots, gradients), then the
+    # step's activations, in the order a training process allocates them
+    expert_w = W.make_expert_weights(wl, args.seed, dev)
+    dup_w = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=expert_w.dtype, device=dev)
+    dup_g, home_g = W.make_grads(wl, args.seed, dev)
     ids_d = torch.from_numpy(ids).to(dev)
     w_d = torch.from_numpy(w).to(dev)
     hidden = W.make_hidden(wl, args.seed, dev)
     recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hidden.dtype, device=dev)
     out = torch.empty_like(hidden)
-    expert_w = W.make_expert_weights(wl, args.seed, dev)
-    dup_w = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=expert_w.dtype, device=dev)
-    dup_g, home_g = W.make_grads(wl, args.seed, dev)
     plan_buf = td.new_plan_buffer(dims, dev)
     if args.with_backward:
         grad_y = torch.empty_like(recv)
