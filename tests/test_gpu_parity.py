@@ -73,6 +73,10 @@ SMALL = [
     _wl("tiles_2048", 8, 64, 8, 8200, 8, 64, W.BF16, 2.0),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
     W.WORKLOADS["tiny"],
+    # an expert with more than 2^21 entries (2 387 355 at seed 0): the bounded
+    # placement's (rows, id) keys no longer pack into one word, and it takes its
+    # three-reduction path; two overflowing experts, pieces on three ranks
+    _wl("big_counts", 4, 8, 2, 600_000, 2, 8, W.BF16, 5.0),
 ]
 
 
