@@ -73,6 +73,12 @@ SMALL = [
     _wl("tiles_2048", 8, 64, 8, 8200, 8, 64, W.BF16, 2.0),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
     W.WORKLOADS["tiny"],
+    # 7 and 16 chunks per lane (rows of 425 or 426 and 1000 16-byte chunks,
+    # ragged), in bf16 and fp32 rows
+    _wl("cpl7_bf16", 4, 16, 4, 300, 4, 3400, W.BF16, 2.0),
+    _wl("cpl7_f32", 2, 8, 2, 400, 2, 1704, W.F32, 2.0),
+    _wl("cpl16_bf16", 2, 8, 4, 250, 2, 8000, W.BF16, 1.5),
+    _wl("cpl16_f32", 2, 8, 2, 500, 2, 4000, W.F32, 2.0),
     # an expert with more than 2^21 entries (2 387 355 at seed 0): the bounded
     # placement's (rows, id) keys no longer pack into one word, and it takes its
     # three-reduction path; two overflowing experts, pieces on three ranks
