@@ -389,6 +389,69 @@ def test_plan_graph_replays(td, bounded):
                           oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded))
 
 
+@PLANS
+def test_whole_step_graph_replays(td, bounded):
+    """Plan, replicate, dispatch, combine and reduce captured in one HIP graph
+    and replayed on new router ids and weights: every replay's outputs equal the
+    oracle's for the inputs it sees. Eager work (input copies, a reset of the
+    home gradients) runs between the replays."""
+    wl = _wl("graph_step", 8, 64, 8, 1000, 8, 64, W.BF16, 2.0)
+    dims = _dims(td, wl)
+    pb = td.new_plan_buffer(dims, DEV)
+    ids0, w0 = W.make_routing(wl, 0)
+    ids_d = torch.from_numpy(ids0).to(DEV)
+    w_d = torch.from_numpy(w0).to(DEV)
+    hidden = W.make_hidden(wl, 5)
+    hid_d = hidden.to(DEV)
+    recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hid_d.dtype, device=DEV)
+    out = torch.empty_like(hid_d)
+    ew = W.make_expert_weights(wl, 5)
+    ew_d = ew.to(DEV)
+    dup_w = torch.zeros((wl.R, wl.B) + tuple(wl.block_shape), dtype=ew.dtype, device=DEV)
+    dg, hg = W.make_grads(wl, 5)
+    dg_d, hg_d = dg.to(DEV), hg.to(DEV)
+    plan_fn = td.moonep_plan_bounded if bounded else td.moonep_plan
+    s = torch.cuda.Stream(DEV)
+
+    def step():
+        plan_fn(dims, ids_d, pb, stream=s)
+        td.moonep_replicate(dims, pb, ew_d, dup_w, wl.block_bytes, stream=s)
+        td.moonep_dispatch(dims, pb, hid_d, recv, stream=s)
+        td.moonep_combine(dims, pb, recv, w_d, out, stream=s)
+        td.moonep_reduce_dup_grads(dims, pb, dg_d, hg_d, wl.block_elems, stream=s)
+
+    with torch.cuda.stream(s):
+        step()  # sets kernel attributes before capture
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    hid_h = _host_rows(hidden).reshape(wl.n_tok, wl.H)
+    ew_h = bf16_bits(ew)
+    for seed in (1, 2, 3, 1):
+        say(f"graph replay bounded={bounded} seed={seed}")
+        ids, w = W.make_routing(wl, seed)
+        ids_d.copy_(torch.from_numpy(ids).to(DEV))
+        w_d.copy_(torch.from_numpy(w).to(DEV))
+        hg_d.copy_(hg.to(DEV))
+        dup_w.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
+        assert_plan_equal(read_plan(td, dims, pb), p)
+        want_recv = oracle.dispatch(p, wl.K, hid_h)
+        assert np.array_equal(_host_rows(recv).reshape(-1, wl.H).view(np.uint16),
+                              want_recv.view(np.uint16)), "dispatch"
+        want_out = oracle.combine(p["dst"], wl.K, want_recv, w, wl.dtype, wl.dtype)
+        assert np.array_equal(_host_rows(out).reshape(-1, wl.H).view(np.uint16),
+                              want_out.view(np.uint16)), "combine"
+        want_w = oracle.replicate(p, wl.B, ew_h)
+        assert np.array_equal(_host_rows(dup_w).view(np.uint16), want_w.view(np.uint16)), "replicate"
+        want_h = oracle.reduce_dup_grads(p, wl.B, dg.numpy(), hg.numpy())
+        assert np.array_equal(f32_bits(hg_d), want_h.view(np.uint32)), "reduce"
+
+
 # ------------------------------------------------------------ full-size shapes
 
 @PLANS
