@@ -21,8 +21,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_common import (assert_plan_equal, bf16_bits, f32_bits, read_plan, run_plan,
-                              say)
+from tests.gpu_common import (PLAN_INT_KEYS, assert_plan_equal, bf16_bits, f32_bits, read_plan,
+                              run_plan, say)
 from tests.invariants import check_plan
 
 pytestmark = pytest.mark.gpu
@@ -450,6 +450,71 @@ def test_whole_step_graph_replays(td, bounded):
         assert np.array_equal(_host_rows(dup_w).view(np.uint16), want_w.view(np.uint16)), "replicate"
         want_h = oracle.reduce_dup_grads(p, wl.B, dg.numpy(), hg.numpy())
         assert np.array_equal(f32_bits(hg_d), want_h.view(np.uint32)), "reduce"
+
+
+def _plans_equal_int32(td, dims, plan_buf, p):
+    """assert_plan_equal without 64-bit copies: the entry-sized arrays at the
+    largest shapes are compared as they are (int32)."""
+    v = td.plan_views(dims, plan_buf)
+    for k in PLAN_INT_KEYS:
+        g = v[k].cpu().numpy().reshape(-1)
+        o = np.asarray(p[k]).reshape(-1)
+        assert g.shape == o.shape and np.array_equal(g, o.astype(np.int32, copy=False)), k
+        del g
+    assert int(v["maxT"][0]) == int(p["maxT"][0])
+    assert v["maxvio"].cpu().numpy().view(np.uint64)[0] == p["maxvio"].view(np.uint64)[0]
+
+
+def test_entries_near_int32_limit(td):
+    """The largest entry count the library takes: R*S*K = 2 147 483 520, just
+    below 2^31 (16 ranks, 64 experts, K = 8, 16 777 215 tokens per rank, 16-byte
+    rows). Both plans are compared with the oracle array by array; dispatch on
+    200 000 sampled slots; combine with identity experts and weights 1/K, whose
+    exact result is the token's own row, on 200 000 sampled tokens."""
+    R, E, K, B, H = 16, 64, 8, 4, 8
+    S = ((1 << 31) - 1) // (R * K)
+    n_ent, n_tok = R * S * K, R * S
+    dims = td.Dims(R, E, K, S, B, W.BF16, H)
+    say(f"near-limit case: {dims}, {n_ent} entries")
+    ids = W.make_consecutive_ids(R, E, K, S, seed=0)
+    say("ids drawn")
+    plan_buf, ids_d = run_plan(td, dims, ids, DEV)
+    say("water-fill plan on the GPU done")
+    p = oracle.plan(R, E, K, S, B, ids)
+    say("oracle water-fill done")
+    _plans_equal_int32(td, dims, plan_buf, p)
+    say(f"water-fill plans equal; duplicates per rank {p['n_dup'].tolist()}")
+
+    hidden = W.dense((R, S, H), W.BF16, 1.0, 0, "hidden", DEV)
+    recv = torch.empty((R, S * K, H), dtype=torch.bfloat16, device=DEV)
+    td.moonep_dispatch(dims, plan_buf, hidden, recv)
+    w_d = torch.full((R, S, K), 1.0 / K, dtype=torch.float32, device=DEV)
+    out = torch.empty_like(hidden)
+    td.moonep_combine(dims, plan_buf, recv, w_d, out)
+    torch.cuda.synchronize()
+    say("dispatch and combine done")
+    rng = np.random.default_rng(3)
+    slots = rng.integers(0, n_ent, 200_000)
+    slots[:2] = (0, n_ent - 1)
+    tok_of_slot = (p["src"][slots].astype(np.int64)) // K
+    got = recv.view(-1, H)[torch.from_numpy(slots).to(DEV)]
+    want = hidden.view(-1, H)[torch.from_numpy(tok_of_slot).to(DEV)]
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "dispatch"
+    toks = rng.integers(0, n_tok, 200_000)
+    toks[:2] = (0, n_tok - 1)
+    tk = torch.from_numpy(toks).to(DEV)
+    assert torch.equal(out.view(-1, H)[tk].view(torch.int16),
+                       hidden.view(-1, H)[tk].view(torch.int16)), "combine"
+    del recv, out, w_d, hidden
+
+    td.moonep_plan_bounded(dims, ids_d, plan_buf)
+    torch.cuda.synchronize()
+    say("bounded plan on the GPU done")
+    del p
+    pb = oracle.plan(R, E, K, S, B, ids, bounded=True)
+    say("oracle bounded plan done")
+    _plans_equal_int32(td, dims, plan_buf, pb)
+    say(f"bounded plans equal; duplicates per rank {pb['n_dup'].tolist()}")
 
 
 # ------------------------------------------------------------ full-size shapes

@@ -169,6 +169,31 @@ def make_routing(wl: Workload, seed: int) -> Tuple[np.ndarray, np.ndarray]:
     return ids.reshape(wl.R, wl.S, K), w.reshape(wl.R, wl.S, K)
 
 
+def make_consecutive_ids(R: int, E: int, K: int, S: int, seed: int,
+                         zipf_s: float = 1.0) -> np.ndarray:
+    """Router ids int32 [R,S,K] that are cheap to draw at billions of entries, for
+    shapes near the largest entry count: token g takes the K experts f_g, f_g + 1,
+    ..., f_g + K - 1 (mod E), distinct as long as K <= E, after a first expert f_g
+    drawn with popularity proportional to rank^-zipf_s over a seeded permutation
+    of the experts. Tokens are drawn in chunks, so the only large array is the
+    result."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(E)
+    pop = np.empty(E, dtype=np.float64)
+    pop[perm] = np.arange(1, E + 1, dtype=np.float64) ** (-zipf_s)
+    cdf = np.cumsum(pop / pop.sum())
+    n = R * S
+    ids = np.empty((n, K), dtype=np.int32)
+    step = np.arange(K, dtype=np.int32)[None, :]
+    for t0 in range(0, n, 1 << 24):
+        m = min(1 << 24, n - t0)
+        first = np.minimum(np.searchsorted(cdf, rng.random(m)), E - 1).astype(np.int32)
+        blk = ids[t0:t0 + m]
+        np.add(first[:, None], step, out=blk)
+        np.remainder(blk, E, out=blk)
+    return ids.reshape(R, S, K)
+
+
 def manifest(*arrays: np.ndarray) -> str:
     """sha256 over the raw bytes of the given host arrays (reproducibility record)."""
     h = hashlib.sha256()
