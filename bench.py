@@ -181,6 +181,7 @@ def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
     import numpy as np
     import torch
     import oracle
+    import workloads as W
 
     t0 = time.perf_counter()
     p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
@@ -197,8 +198,10 @@ def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
 
     def gather(n):
         dsel = p["dst"][:n * wl.K].astype(np.int64)
-        return y_dev.view(-1, wl.H)[torch.from_numpy(dsel).to(y_dev.device)].cpu() \
-            .view(torch.int16).numpy().view(np.uint16)
+        rows = y_dev.view(-1, wl.H)[torch.from_numpy(dsel).to(y_dev.device)].cpu()
+        if wl.dtype == W.BF16:
+            return rows.view(torch.int16).numpy().view(np.uint16)
+        return rows.numpy()
 
     def comb(n, y_rows):
         t0 = time.perf_counter()

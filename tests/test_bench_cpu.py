@@ -97,3 +97,19 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("name,dt", [("tiny", None), ("tiny", W.BF16)])
+def test_cpu_baseline_runs_on_host_tensors(name, dt):
+    """The CPU-baseline leg on host tensors, with fp32 rows (the tiny workload as
+    given) and bf16 rows: it times the oracle and reports a positive rate."""
+    import torch
+    wl = W.WORKLOADS[name]
+    if dt is not None:
+        wl = wl.replace(dtype=dt)
+    ids, w = W.make_routing(wl, 0)
+    hidden = W.make_hidden(wl, 0)
+    recv = torch.zeros((wl.R, wl.SK, wl.H), dtype=hidden.dtype)
+    rec = bench.cpu_baseline(wl, ids, w, hidden, recv, 0.2)
+    assert rec["value"] > 0 and rec["cores"] == 1 and rec["kind"] == "oracle"
+    assert "destination-rank windows" in rec["sample"]
