@@ -196,24 +196,29 @@ def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
         ranks += 1
     del hid
 
-    def gather(n):
-        dsel = p["dst"][:n * wl.K].astype(np.int64)
+    def gather(t0, n):
+        dsel = p["dst"][t0 * wl.K:(t0 + n) * wl.K].astype(np.int64)
         rows = y_dev.view(-1, wl.H)[torch.from_numpy(dsel).to(y_dev.device)].cpu()
         if wl.dtype == W.BF16:
             return rows.view(torch.int16).numpy().view(np.uint16)
         return rows.numpy()
 
-    def comb(n, y_rows):
-        t0 = time.perf_counter()
+    def comb(t0, n, y_rows):
+        t0w = time.perf_counter()
         oracle.combine(np.arange(n * wl.K, dtype=np.int32), wl.K, y_rows,
-                       w.reshape(-1)[:n * wl.K], wl.dtype, wl.dtype)
-        return time.perf_counter() - t0
+                       w.reshape(-1)[t0 * wl.K:(t0 + n) * wl.K], wl.dtype, wl.dtype)
+        return time.perf_counter() - t0w
 
-    probe = min(64, wl.n_tok)
-    per_tok = comb(probe, gather(probe)) / probe
+    # consecutive batches of at most 8192 tokens (bounded host memory for the
+    # gathered rows) until the rest of the budget is spent or every token is done
     left = max(0.0, budget_s - t_plan - t_disp)
-    n = int(min(wl.n_tok, 8192, max(probe, left / max(per_tok, 1e-9))))
-    t_comb = comb(n, gather(n))
+    t_comb, n = 0.0, 0
+    while n < wl.n_tok and (n == 0 or t_comb < left):
+        m = min(8192, wl.n_tok - n)
+        rows = gather(n, m)
+        t_comb += comb(n, m, rows)
+        n += m
+        del rows
 
     nbytes = algorithmic_bytes(wl, 0, 0)
     t_d_full = t_disp / ranks * wl.R
