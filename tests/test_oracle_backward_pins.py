@@ -145,3 +145,17 @@ def test_dispatch_backward_of_dispatch_is_k_times_hidden(K):
     recv = oracle.dispatch(p, K, hidden)
     back = oracle.dispatch_backward(p["dst"], K, recv, oracle.BF16, oracle.BF16)
     assert np.array_equal(back, _bf16_bits(K * _as_f32(hidden, oracle.BF16)))
+
+
+@pytest.mark.parametrize("out_dt", [oracle.F32, oracle.BF16])
+def test_dispatch_backward_sum_starts_from_positive_zero(out_dt):
+    """The backward of dispatch adds from +0.0 (the reading of its definition).
+    A token whose K entries are all dropped then gets +0.0, and so does a token
+    whose every slot gradient is -0.0, because (+0) + (-0) = +0 when rounding to
+    nearest; a -0.0 start would give -0.0 in both cases."""
+    K, H = 2, 4
+    dst = np.array([-1, -1, 0, 1], dtype=np.int32)  # token 0 dropped, token 1 in slots 0 and 1
+    grec = np.full((2, H), -0.0, dtype=np.float32)
+    gh = oracle.dispatch_backward(dst, K, grec, oracle.F32, out_dt)
+    bits = gh.view(np.uint32) if out_dt == oracle.F32 else gh.view(np.uint16)
+    assert not np.any(bits)

@@ -95,6 +95,33 @@ MUTANTS = [
      "                if (d < 0) continue;\n                acc = acc +",
      "for (int k = 1; k < K; ++k) {\n                int64_t d = dst[g * K + k];\n"
      "                if (d < 0) continue;\n                acc = acc +", 0),
+    ("duplicate_start_one_late", [PINS],
+     "o->dup_start[(int64_t)r * dcap + nd] = (int32_t)s0;",
+     "o->dup_start[(int64_t)r * dcap + nd] = (int32_t)(s0 + 1);", 0),
+    ("duplicate_count_one_short", [PINS],
+     "o->dup_count[(int64_t)r * dcap + nd] = (int32_t)(s - s0);",
+     "o->dup_count[(int64_t)r * dcap + nd] = (int32_t)(s - s0 - 1);", 0),
+    ("segment_end_at_kept_rows", [PINS],
+     "o->seg_ptr[r * sp + G + o->n_dup[r]] = (int32_t)end;",
+     "o->seg_ptr[r * sp + G + o->n_dup[r]] = (int32_t)o->keep[r];", 0),
+    ("duplicate_csr_end_short", [PINS], "o->dup_ptr[E] = p;", "o->dup_ptr[E] = p > 0 ? p - 1 : 0;", 0),
+    ("bad_id_not_reported", [PINS],
+     "if (e < 0 || e >= E) { status |= ST_BAD_ID; continue; }",
+     "if (e < 0 || e >= E) { continue; }", 0),
+    ("grad_w_in_binary32", [BACKWARD], "double s = 0.0;", "float s = 0.0f;", 0),
+    ("dispatch_backward_from_negative_zero", [BACKWARD],
+     "float acc = 0.0f;\n            for (int k = 0; k < K; ++k) {\n"
+     "                int64_t d = dst[g * K + k];\n                if (d < 0) continue;\n"
+     "                acc = acc +",
+     "float acc = -0.0f;\n            for (int k = 0; k < K; ++k) {\n"
+     "                int64_t d = dst[g * K + k];\n                if (d < 0) continue;\n"
+     "                acc = acc +", 0),
+    ("grad_y_not_rounded_to_bf16", [BACKWARD],
+     "if (dtype == DT_BF16) ((uint16_t *)base)[idx] = f32_to_bf16_rne(v);",
+     "if (dtype == DT_BF16) { uint32_t u; memcpy(&u, &v, 4); ((uint16_t *)base)[idx] = (uint16_t)(u >> 16); }", 0),
+    ("bounded_bad_id_not_reported", [BOUNDED],
+     "if (e < 0 || e >= E) { status |= ST_BAD_ID; continue; }",
+     "if (e < 0 || e >= E) { continue; }", 1),
     ("bounded_overflow_from_smallest", [BOUNDED],
      "(best < 0 || o->T[r * G + i] > o->T[r * G + best])",
      "(best < 0 || o->T[r * G + i] < o->T[r * G + best])", 0),
