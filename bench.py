@@ -159,6 +159,30 @@ def plan_latency(plan_fn, dims, ids_d, plan_buf, stream, iters):
     return out
 
 
+def graph_replay(step, stream, steps):
+    """The whole step captured once in a HIP graph (every chunk launch a kernel
+    node) and replayed `steps` times: milliseconds per replay by events on the
+    launch stream, or the reason the capture failed."""
+    import torch
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            g.replay()
+        b.record(stream)
+        b.synchronize()
+        return {"ms_per_step": round(a.elapsed_time(b) / steps, 4), "replays": steps}
+    except Exception as exc:  # report, do not lose the bench line
+        return {"error": f"{type(exc).__name__}: {exc}"}
+
+
 def host_cpu() -> str:
     """The host's CPU model and logical CPU count, as the baseline's context."""
     model = "unknown CPU"
@@ -250,6 +274,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (graph_ms_per_step)")
     ap.add_argument("--with-backward", action="store_true",
                     help="also time combine-backward (grad_out = out, y = recv) and "
                          "dispatch-backward (grad_recv = grad_y) in every step")
@@ -361,6 +387,10 @@ def main():
     op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, op in enumerate(ops)}
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    graph = None
+    if not args.no_graph and not args.copy_calibration:
+        graph = graph_replay(step, stream, args.steps)
+        print(f"# graph replay: {graph}", file=sys.stderr, flush=True)
     plan_lat = None
     if args.plan_iters > 0 and not args.copy_calibration:
         plan_lat = plan_latency(plan_fn, dims, ids_d, plan_buf, stream, args.plan_iters)
@@ -427,6 +457,7 @@ def main():
                    "parallelism": "ep (virtual, 1 GPU)"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "plan_us": round(op_ms["plan"] * 1e3, 2), "plan_latency_us": plan_lat,
+        "graph": graph,
         "op_ms": {k: round(x, 4) for k, x in op_ms.items()},
         "op_gbs": {k: round(x, 1) for k, x in gbs.items()},
         "maxvio_before": round(maxvio, 4), "rank_maxvio_after": rank_maxvio_after,
