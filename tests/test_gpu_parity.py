@@ -239,6 +239,21 @@ def test_invalid_and_repeated_ids(td, bounded):
 
 
 @PLANS
+def test_every_id_dropped(td, bounded):
+    """The degenerate step with no valid assignment: every id out of range. The
+    plan has T = 0, no overflow and no duplicates, every slot stays empty, combine
+    gives +0 everywhere, and replicate and reduce touch nothing."""
+    wl = _wl("all_dropped", 4, 32, 4, 600, 4, 64, W.BF16, 2.0)
+    _, w = W.make_routing(wl, seed=9)
+    for fill in (-1, wl.E):
+        ids = np.full(wl.n_ent, fill, dtype=np.int32)
+        g = _full_case(td, wl, ids, w.reshape(-1), 9, bounded)
+        assert int(g["status"][0]) & 1
+        assert not np.any(g["T"]) and not np.any(g["n_dup"])
+        assert np.all(g["dst"] == -1) and np.all(g["src"] == -1)
+
+
+@PLANS
 def test_repeated_ids_several_tokens_per_thread(td, bounded):
     # K = 2 and 512 tokens per 1024-entry tile: counting thread t takes tokens
     # t and t + 256 of its tile in turn, so its per-token seen set must be
