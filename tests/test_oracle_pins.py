@@ -218,6 +218,23 @@ def test_invalid_and_repeated_ids():
         assert bool(st & oracle.ST_REPEAT_ID) == (trial % 2 == 1)
 
 
+@pytest.mark.parametrize("bounded", [False, True])
+def test_every_id_dropped_closed_form(bounded):
+    """No valid assignment at all: T = 0, maxvio = 0 * E / (R*S*K) - 1 = -1, every
+    rank keeps nothing and has a deficit of S*K, nothing overflows, every entry
+    and every slot is empty, and the bad-id bit is set."""
+    R, E, K, S = 3, 9, 2, 7
+    for fill in (-1, E, -5):
+        ids = np.full(R * S * K, fill, dtype=np.int32)
+        p = oracle.plan(R, E, K, S, 2, ids, bounded=bounded)
+        assert not np.any(p["T"]) and float(p["maxvio"][0]) == -1.0
+        assert not np.any(p["L"]) and not np.any(p["keep"]) and not np.any(p["O"])
+        assert np.all(p["D"] == S * K) and p["Dpre"].tolist() == [r * S * K for r in range(R + 1)]
+        assert np.all(p["dst"] == -1) and np.all(p["src"] == -1)
+        assert not np.any(p["n_dup"]) and int(p["n_list"][0]) == 0
+        assert int(p["status"][0]) == oracle.ST_BAD_ID
+
+
 # ------------------------------------------------------------------ data moves
 
 def _bf16_bits(x):
