@@ -467,6 +467,39 @@ def test_whole_step_graph_replays(td, bounded):
         assert np.array_equal(f32_bits(hg_d), want_h.view(np.uint32)), "reduce"
 
 
+def test_rows_past_the_buffer_range(td):
+    """Rows of 2 GiB (H = 2^30 bf16): combine and the backward of dispatch read
+    them with global loads instead of through a buffer resource, whose 32-bit
+    range they exceed. Two tokens, one expert each, both paths checked against
+    the oracle on every element."""
+    R, E, K, S, B, H = 1, 2, 1, 2, 1, 1 << 30
+    dims = td.Dims(R, E, K, S, B, W.BF16, H)
+    say(f"2 GiB rows: {dims}")
+    ids = np.array([1, 0], dtype=np.int32)
+    plan_buf, _ = run_plan(td, dims, ids, DEV)
+    p = oracle.plan(R, E, K, S, B, ids)
+    assert_plan_equal(read_plan(td, dims, plan_buf), p)
+    hidden = W.dense((R, S, H), W.BF16, 1.0, 3, "hidden", DEV)
+    recv = torch.empty((R, S * K, H), dtype=torch.bfloat16, device=DEV)
+    td.moonep_dispatch(dims, plan_buf, hidden, recv)
+    w = np.array([0.75, -1.25], dtype=np.float32)
+    out = torch.empty_like(hidden)
+    td.moonep_combine(dims, plan_buf, recv, torch.from_numpy(w).to(DEV), out)
+    back = torch.empty_like(hidden)
+    td.moonep_dispatch_backward(dims, plan_buf, recv, back, W.BF16)
+    torch.cuda.synchronize()
+    say("  kernels done")
+    hid_h = bf16_bits(hidden).reshape(S, H)
+    del hidden
+    want_recv = oracle.dispatch(p, K, hid_h)
+    assert np.array_equal(bf16_bits(recv).reshape(S, H), want_recv), "dispatch"
+    want_out = oracle.combine(p["dst"], K, want_recv, w, W.BF16, W.BF16)
+    assert np.array_equal(bf16_bits(out).reshape(S, H), want_out), "combine"
+    del out
+    want_back = oracle.dispatch_backward(p["dst"], K, want_recv, W.BF16, W.BF16)
+    assert np.array_equal(bf16_bits(back).reshape(S, H), want_back), "dispatch backward"
+
+
 def _plans_equal_int32(td, dims, plan_buf, p):
     """assert_plan_equal without 64-bit copies: the entry-sized arrays at the
     largest shapes are compared as they are (int32)."""

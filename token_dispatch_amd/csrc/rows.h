@@ -38,6 +38,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
 
+// Rows read through a buffer resource: the row's base address and length sit in
+// scalar registers and each lane only supplies a 32-bit byte offset, so a row
+// load needs no 64-bit address arithmetic per lane. Offsets at or past the
+// length read 0 (the hardware range check). A row qualifies when every lane's
+// byte offset, including the lanes past the row's end in its last segment (at
+// most 64 * 16 chunks further), stays below 2^31.
+constexpr int64_t kBufRowChunks = (((int64_t)1 << 31) - ((int64_t)1 << 16)) / 16;
+constexpr int kWordFormat = 0x00020000;  // raw (untyped) buffer of 32-bit words
+constexpr int kPolicyNT = 2;             // non-temporal: each byte is read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const v4u *row, int32_t chunks) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u *>(row), (short)0, chunks * 16,
+                                             kWordFormat);
+}
+
+__device__ __forceinline__ v4u load_chunk_nt(__amdgpu_buffer_rsrc_t rs, int c) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, kPolicyNT);
+}
+
 // One 16-byte chunk of a row as binary32 values: 8 bf16 or 4 f32.
 template <bool IN_BF16>
 struct Chunk;
