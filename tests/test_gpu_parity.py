@@ -338,6 +338,46 @@ def test_deterministic_and_stream_ordered(td):
         assert_plan_equal(read_plan(td, dims, pb), a)
 
 
+def test_two_streams_at_once(td):
+    """The library keeps no state between calls: two independent steps (plan,
+    dispatch, combine) enqueued on two streams and running concurrently, with
+    different shapes and routings, each match the oracle."""
+    cases = [_wl("stream_a", 8, 64, 8, 1500, 8, 256, W.BF16, 2.0),
+             _wl("stream_b", 4, 32, 4, 2500, 4, 128, W.F32, 1.5)]
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    runs = []
+    for wl, s, seed in zip(cases, streams, (11, 12)):
+        dims = _dims(td, wl)
+        ids, w = W.make_routing(wl, seed)
+        hidden = W.make_hidden(wl, seed)
+        with torch.cuda.stream(s):
+            ids_d = torch.from_numpy(ids).to(DEV)
+            w_d = torch.from_numpy(w).to(DEV)
+            hid_d = hidden.to(DEV)
+            pb = td.new_plan_buffer(dims, DEV)
+            recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hid_d.dtype, device=DEV)
+            out = torch.empty_like(hid_d)
+        runs.append((wl, dims, ids, w, hidden, ids_d, w_d, hid_d, pb, recv, out, s))
+    torch.cuda.synchronize()
+    for _ in range(3):  # interleaved enqueues on both streams
+        for wl, dims, ids, w, hidden, ids_d, w_d, hid_d, pb, recv, out, s in runs:
+            td.moonep_plan(dims, ids_d, pb, stream=s)
+        for wl, dims, ids, w, hidden, ids_d, w_d, hid_d, pb, recv, out, s in runs:
+            td.moonep_dispatch(dims, pb, hid_d, recv, stream=s)
+            td.moonep_combine(dims, pb, recv, w_d, out, stream=s)
+    torch.cuda.synchronize()
+    for wl, dims, ids, w, hidden, ids_d, w_d, hid_d, pb, recv, out, s in runs:
+        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+        assert_plan_equal(read_plan(td, dims, pb), p)
+        hid_h = _host_rows(hidden).reshape(wl.n_tok, wl.H)
+        want_recv = oracle.dispatch(p, wl.K, hid_h)
+        assert np.array_equal(_host_rows(recv).reshape(-1, wl.H).view(np.uint8),
+                              want_recv.view(np.uint8)), wl.name
+        want_out = oracle.combine(p["dst"], wl.K, want_recv, w, wl.dtype, wl.dtype)
+        assert np.array_equal(_host_rows(out).reshape(-1, wl.H).view(np.uint8),
+                              want_out.view(np.uint8)), wl.name
+
+
 def test_plan_buffer_reuse_across_shapes(td):
     """A plan buffer first used for a larger problem gives the same plan for a
     smaller one (no stale state leaks into the result)."""
