@@ -26,6 +26,8 @@
  *     written on the device; the caller reads it when it chooses to synchronise.
  *   - Calls that share a plan buffer must be ordered (same stream, or events).
  *     Calls on different plan buffers and outputs are independent.
+ *   - The calls that take a plan (the moves and their backward) read only its
+ *     first moonep_layout.persist_bytes bytes.
  */
 #ifndef MOONEP_H
 #define MOONEP_H
@@ -107,10 +109,16 @@ typedef struct moonep_dims {
  *                                  (expert, rank); -1 beyond n_list
  *   dup_ptr     int32 [E+1]        CSR of that list over experts
  * The remaining offsets are workspace of the plan kernels; callers must not
- * rely on their contents.
+ * rely on their contents. Workspace that later calls read (ws_mat_pre, ws_xlist,
+ * ws_n_x) lies below persist_bytes; scratch used only while the plan kernels run
+ * (ws_tile_counts, ws_tile_status, ws_piece_js, ws_kept, ws_koff, ws_upre,
+ * ws_pslot, ws_pcnt) lies in [persist_bytes, bytes).
  */
 typedef struct moonep_layout {
     int64_t bytes;
+    int64_t persist_bytes; /* the arrays above and the workspace later calls read lie in
+                              [0, persist_bytes); [persist_bytes, bytes) is scratch that
+                              only the plan call itself uses (see moonep_plan_noscratch) */
     int32_t dcap;          /* max(1, min(SK, E - G)): most duplicates one rank can hold */
     int32_t pcap;          /* E + R: room for the global duplicate list                 */
     int32_t n_tiles;       /* token tiles of the plan kernels                           */
@@ -176,6 +184,40 @@ int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf
  */
 int moonep_plan_bounded(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf,
                         void *stream);
+
+/*
+ * moonep_plan_noscratch -- moonep_plan (bounded = 0) or moonep_plan_bounded
+ * (bounded = 1) for callers that cannot allocate device memory and cannot give
+ * the plan room for its scratch: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.
+ *
+ *   topk_ids  as moonep_plan
+ *   plan_buf  device buffer of at least moonep_plan_layout().persist_bytes bytes,
+ *             written exactly as moonep_plan writes the same offsets; every later
+ *             call (dispatch, replicate, combine, reduce, the backward moves) takes
+ *             it as a plan buffer of the full size
+ *   bounded   0 or 1 (anything else: MOONEP_ERR_DIMS)
+ *
+ * The plan kernels' scratch, bytes - persist_bytes of it, lives in one array of
+ * MOONEP_STATIC_SCRATCH_BYTES in the library's device memory instead of the tail
+ * of plan_buf. Each GPU holds its own copy of that array from the first call on
+ * it until the process ends. Nothing is allocated or freed by the call.
+ *   - A problem whose scratch exceeds MOONEP_STATIC_SCRATCH_BYTES returns
+ *     MOONEP_ERR_SIZE before anything is enqueued. The scratch is about
+ *     4 * E * n_tiles bytes (n_tiles from moonep_plan_layout): 1.9 MB at
+ *     R = 32, E = 896, K = 16, S = 4096; 0.5 MB at R = 64, S = 128.
+ *   - Every call on one GPU shares that GPU's array: two calls whose kernels may
+ *     run at the same time on one GPU (different streams without ordering between
+ *     them) race on it and give undefined plans. Calls ordered on one stream are
+ *     safe; the kernels write the scratch before they read it, so the contents a
+ *     previous call left behind never matter.
+ *   - The first call on a GPU looks up the array's device address
+ *     (hipGetSymbolAddress); a failure there returns MOONEP_ERR_HIP.
+ * Results are bit-for-bit those of moonep_plan / moonep_plan_bounded.
+ */
+#define MOONEP_STATIC_SCRATCH_BYTES (8u << 20)
+int moonep_plan_noscratch(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf,
+                          int32_t bounded, void *stream);
 
 /*
  * moonep_dispatch -- zero-copy scatter of token rows into the static,

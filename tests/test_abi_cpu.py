@@ -69,6 +69,15 @@ def test_layout(td, shape):
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):
         assert a0 % 256 == 0 and a1 <= b0
     assert spans[-1][1] <= lay.bytes
+    # what later calls read lies below persist_bytes, the plan kernels' own scratch above
+    scratch = {"ws_tile_counts", "ws_tile_status", "ws_piece_js", "ws_kept", "ws_koff",
+               "ws_upre", "ws_pslot", "ws_pcnt"}
+    assert lay.persist_bytes % 256 == 0 and 0 < lay.persist_bytes < lay.bytes
+    for k, v in sizes.items():
+        if k in scratch:
+            assert getattr(lay, k) >= lay.persist_bytes, k
+        else:
+            assert getattr(lay, k) + v <= lay.persist_bytes, k
     # same dims, same layout (static shapes)
     assert td.moonep_plan_layout(td.Dims(*shape)).bytes == lay.bytes
 
@@ -120,6 +129,27 @@ def test_pointer_and_size_errors(td):
                                    ctypes.byref(n)) == -1
     for rc in (0, -1, -2, -3, -4, 5):
         assert td.moonep_strerror(rc)
+
+
+def test_noscratch_argument_errors(td):
+    """moonep_plan_noscratch rejects, before touching any device, a bounded flag
+    other than 0 or 1, bad pointers, and problems whose scratch does not fit the
+    static array."""
+    lib = td._lib
+    ok = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    d = _dims(td)
+    lay = td.moonep_plan_layout(d)
+    assert lay.bytes - lay.persist_bytes <= td.STATIC_SCRATCH_BYTES
+    assert lib.moonep_plan_noscratch(ctypes.byref(d), ok, ok, 2, None) == -1
+    assert lib.moonep_plan_noscratch(ctypes.byref(d), ok, mis, 0, None) == -2
+    assert lib.moonep_plan_noscratch(ctypes.byref(d), None, ok, 1, None) == -2
+    assert lib.moonep_plan_noscratch(ctypes.byref(_dims(td, E=900)), ok, ok, 0, None) == -1
+    # 8192 tiles of 4096 entries x 1024 experts of counts: 32 MiB of scratch
+    big = td.Dims(64, 1024, 8, 65536, 4, 1, 64)
+    lb = td.moonep_plan_layout(big)
+    assert lb.bytes - lb.persist_bytes > td.STATIC_SCRATCH_BYTES
+    assert lib.moonep_plan_noscratch(ctypes.byref(big), ok, ok, 0, None) == -4
 
 
 def test_binding_checks_tensors(td):

@@ -27,11 +27,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 F32 = 0
 BF16 = 1
+STATIC_SCRATCH_BYTES = 8 << 20  # MOONEP_STATIC_SCRATCH_BYTES
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 OP_DISPATCH, OP_COMBINE = 1, 2
 
-ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded", "moonep_dispatch",
-                "moonep_replicate",
+ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded",
+                "moonep_plan_noscratch", "moonep_dispatch", "moonep_replicate",
                 "moonep_combine", "moonep_reduce_dup_grads", "moonep_combine_backward",
                 "moonep_dispatch_backward", "moonep_launch_count", "moonep_strerror")
 
@@ -57,7 +58,8 @@ _LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D
 
 
 class Layout(ctypes.Structure):
-    _fields_ = ([("bytes", ctypes.c_int64), ("dcap", ctypes.c_int32), ("pcap", ctypes.c_int32),
+    _fields_ = ([("bytes", ctypes.c_int64), ("persist_bytes", ctypes.c_int64),
+                 ("dcap", ctypes.c_int32), ("pcap", ctypes.c_int32),
                  ("n_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32)]
                 + [(n, ctypes.c_int64) for n in _LAYOUT_OFFSETS])
 
@@ -67,6 +69,7 @@ _P_DIMS, _P_LAY = ctypes.POINTER(Dims), ctypes.POINTER(Layout)
 _lib.moonep_plan_layout.argtypes = [_P_DIMS, _P_LAY]
 _lib.moonep_plan.argtypes = [_P_DIMS, _vp, _vp, _vp]
 _lib.moonep_plan_bounded.argtypes = [_P_DIMS, _vp, _vp, _vp]
+_lib.moonep_plan_noscratch.argtypes = [_P_DIMS, _vp, _vp, _i32, _vp]
 _lib.moonep_dispatch.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp]
 _lib.moonep_replicate.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
 _lib.moonep_combine.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp, _i32, _vp]
@@ -158,12 +161,24 @@ def moonep_plan_bounded(dims: Dims, topk_ids, plan_buf, stream=None) -> None:
            "moonep_plan_bounded")
 
 
+def moonep_plan_noscratch(dims: Dims, topk_ids, plan_buf, bounded: bool = False,
+                          stream=None) -> None:
+    """moonep_plan (or moonep_plan_bounded) with the plan kernels' scratch in the
+    library's static device array: plan_buf needs only persist_bytes bytes."""
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    ids = _ptr(topk_ids, "topk_ids", torch.int32, 4 * dims.R * dims.S * dims.K)
+    pb = _ptr(plan_buf, "plan_buf", None, lay.persist_bytes)
+    _check(_lib.moonep_plan_noscratch(ctypes.byref(dims), ids, pb, 1 if bounded else 0,
+                                      _stream(stream, plan_buf)), "moonep_plan_noscratch")
+
+
 def moonep_dispatch(dims: Dims, plan_buf, hidden, recv, stream=None) -> None:
     dt = _row_dtype(dims)
     row = dims.H * (2 if dims.dtype == BF16 else 4)
     lay = moonep_plan_layout(dims)
     _check(_lib.moonep_dispatch(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(hidden, "hidden", dt, dims.R * dims.S * row),
         _ptr(recv, "recv", dt, dims.R * dims.S * dims.K * row),
         _stream(stream, recv)), "moonep_dispatch")
@@ -172,7 +187,7 @@ def moonep_dispatch(dims: Dims, plan_buf, hidden, recv, stream=None) -> None:
 def moonep_replicate(dims: Dims, plan_buf, expert_w, dup_w, block_bytes: int, stream=None) -> None:
     lay = moonep_plan_layout(dims)
     _check(_lib.moonep_replicate(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(expert_w, "expert_w", None, dims.E * block_bytes),
         _ptr(dup_w, "dup_w", None, dims.R * dims.B * block_bytes),
         int(block_bytes), _stream(stream, dup_w)), "moonep_replicate")
@@ -186,7 +201,7 @@ def moonep_combine(dims: Dims, plan_buf, y, topk_w, out, out_dtype: Optional[int
     orow = dims.H * (2 if od == BF16 else 4)
     lay = moonep_plan_layout(dims)
     _check(_lib.moonep_combine(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(y, "y", _row_dtype(dims), dims.R * dims.S * dims.K * row),
         _ptr(topk_w, "topk_w", torch.float32, 4 * dims.R * dims.S * dims.K),
         _ptr(out, "out", torch.bfloat16 if od == BF16 else torch.float32, dims.R * dims.S * orow),
@@ -198,7 +213,7 @@ def moonep_reduce_dup_grads(dims: Dims, plan_buf, dup_grads, home_grads, block_e
     torch = _torch()
     lay = moonep_plan_layout(dims)
     _check(_lib.moonep_reduce_dup_grads(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(dup_grads, "dup_grads", torch.float32, 4 * dims.R * dims.B * block_elems),
         _ptr(home_grads, "home_grads", torch.float32, 4 * dims.E * block_elems),
         int(block_elems), _stream(stream, home_grads)), "moonep_reduce_dup_grads")
@@ -216,7 +231,7 @@ def moonep_combine_backward(dims: Dims, plan_buf, grad_out, topk_w, y, grad_y, g
     lay = moonep_plan_layout(dims)
     ref = grad_y if grad_y is not None else grad_out
     _check(_lib.moonep_combine_backward(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(grad_out, "grad_out", None, dims.R * dims.S * grow), g_dt,
         None if grad_y is None else _ptr(topk_w, "topk_w", torch.float32, 4 * n_ent),
         None if grad_w is None else _ptr(y, "y", _row_dtype(dims), n_ent * row),
@@ -233,7 +248,7 @@ def moonep_dispatch_backward(dims: Dims, plan_buf, grad_recv, grad_hidden,
     orow = dims.H * (2 if od == BF16 else 4)
     lay = moonep_plan_layout(dims)
     _check(_lib.moonep_dispatch_backward(
-        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.bytes),
+        ctypes.byref(dims), _ptr(plan_buf, "plan_buf", None, lay.persist_bytes),
         _ptr(grad_recv, "grad_recv", _row_dtype(dims), dims.R * dims.S * dims.K * row),
         _ptr(grad_hidden, "grad_hidden", torch.bfloat16 if od == BF16 else torch.float32,
              dims.R * dims.S * orow), od, _stream(stream, grad_hidden)), "moonep_dispatch_backward")
@@ -245,11 +260,13 @@ def dims_of(R: int, E: int, K: int, S: int, B: int, H: int, dtype: int) -> Dims:
     return Dims(R, E, K, S, B, dtype, H)
 
 
-def new_plan_buffer(dims: Dims, device="cuda"):
-    """A device buffer of the size the plan layout asks for."""
+def new_plan_buffer(dims: Dims, device="cuda", persistent_only: bool = False):
+    """A device buffer of the size the plan layout asks for (persistent_only: only
+    the part that outlives the plan call, enough for moonep_plan_noscratch)."""
     torch = _torch()
     lay = moonep_plan_layout(dims)
-    return torch.empty(lay.bytes, dtype=torch.uint8, device=device)
+    n = lay.persist_bytes if persistent_only else lay.bytes
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def plan_views(dims: Dims, plan_buf) -> Dict[str, "torch.Tensor"]:

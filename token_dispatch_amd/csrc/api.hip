@@ -2,7 +2,17 @@
 // launches on the caller's stream. No call allocates, frees or synchronises.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
+
+// The plan kernels' scratch for moonep_plan_noscratch: one array per GPU in the
+// library's device memory, held from the first use on a GPU until the process
+// ends. In host code the name is only a stand-in, never a device address: the
+// address is looked up once per device (static_scratch below) and that pointer
+// is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[MOONEP_STATIC_SCRATCH_BYTES];
 
 namespace moonep {
 namespace {
@@ -55,10 +65,43 @@ PlanShape shape_of(const moonep_dims *d, const moonep_layout &lay) {
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP; }
 
+// Device address of `scratch` on the current device, looked up with
+// hipGetSymbolAddress on the first call made with that device current and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int static_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOONEP_ERR_HIP;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+                (void)hipGetLastError();
+                return MOONEP_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return MOONEP_OK;
+}
+
 }  // namespace
 
 PlanPtrs resolve(const moonep_layout &l, void *base) {
+    return resolve(l, base, static_cast<char *>(base) + l.persist_bytes);
+}
+
+PlanPtrs resolve(const moonep_layout &l, void *base, void *scratch_base) {
     auto at = [base](int64_t off) { return reinterpret_cast<int32_t *>(static_cast<char *>(base) + off); };
+    // offsets at or past persist_bytes are taken from scratch_base instead
+    auto sc = [&l, scratch_base](int64_t off) {
+        return reinterpret_cast<int32_t *>(static_cast<char *>(scratch_base) + (off - l.persist_bytes));
+    };
     PlanPtrs p;
     p.status = at(l.status);
     p.maxT = at(l.maxT);
@@ -84,17 +127,17 @@ PlanPtrs resolve(const moonep_layout &l, void *base) {
     p.list_rank = at(l.list_rank);
     p.list_b = at(l.list_b);
     p.dup_ptr = at(l.dup_ptr);
-    p.tile_counts = at(l.ws_tile_counts);
-    p.tile_status = at(l.ws_tile_status);
     p.mat_pre = at(l.ws_mat_pre);
     p.xlist = at(l.ws_xlist);
     p.n_x = at(l.ws_n_x);
-    p.piece_js = at(l.ws_piece_js);
-    p.kept = at(l.ws_kept);
-    p.koff = at(l.ws_koff);
-    p.upre = at(l.ws_upre);
-    p.pslot = at(l.ws_pslot);
-    p.pcnt = at(l.ws_pcnt);
+    p.tile_counts = sc(l.ws_tile_counts);
+    p.tile_status = sc(l.ws_tile_status);
+    p.piece_js = sc(l.ws_piece_js);
+    p.kept = sc(l.ws_kept);
+    p.koff = sc(l.ws_koff);
+    p.upre = sc(l.ws_upre);
+    p.pslot = sc(l.ws_pslot);
+    p.pcnt = sc(l.ws_pcnt);
     return p;
 }
 
@@ -152,11 +195,14 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     l.list_rank = take(4 * (int64_t)l.pcap);
     l.list_b = take(4 * (int64_t)l.pcap);
     l.dup_ptr = take(4 * (E + 1));
-    l.ws_tile_counts = take(4 * (int64_t)l.n_tiles * E);
-    l.ws_tile_status = take(4 * (int64_t)l.n_tiles);
+    // workspace that later calls read (replicate: mat_pre; reduce: xlist, n_x)
     l.ws_mat_pre = take(4 * (R + 1));
     l.ws_xlist = take(4 * E);
     l.ws_n_x = take(4);
+    l.persist_bytes = off;
+    // scratch of the plan kernels alone, last, so that it can live elsewhere
+    l.ws_tile_counts = take(4 * (int64_t)l.n_tiles * E);
+    l.ws_tile_status = take(4 * (int64_t)l.n_tiles);
     l.ws_piece_js = take(4 * (int64_t)l.pcap);
     l.ws_kept = take(4 * E);
     l.ws_koff = take(4 * E);
@@ -187,6 +233,23 @@ int moonep_plan(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, v
 int moonep_plan_bounded(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf,
                         void *stream) {
     return plan_common(d, topk_ids, plan_buf, stream, true);
+}
+
+int moonep_plan_noscratch(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf,
+                          int32_t bounded, void *stream) {
+    moonep_layout l;
+    int rc = moonep_plan_layout(d, &l);
+    if (rc != MOONEP_OK) return rc;
+    if (bounded != 0 && bounded != 1) return MOONEP_ERR_DIMS;
+    if (!aligned16(topk_ids) || !aligned16(plan_buf)) return MOONEP_ERR_PTR;
+    if (l.bytes - l.persist_bytes > (int64_t)MOONEP_STATIC_SCRATCH_BYTES) return MOONEP_ERR_SIZE;
+    void *scr = nullptr;
+    rc = static_scratch(&scr);
+    if (rc != MOONEP_OK) return rc;
+    const PlanShape sh = shape_of(d, l);
+    (void)hipGetLastError();
+    return launch_rc(launch_plan(sh, topk_ids, resolve(l, plan_buf, scr), bounded != 0,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int moonep_dispatch(const moonep_dims *d, const void *plan_buf, const void *hidden, void *recv,

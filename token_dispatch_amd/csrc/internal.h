@@ -45,7 +45,10 @@ struct PlanShape {
     float inv_k;          // 1/K rounded to nearest: token of an in-tile entry index
 };
 
+// Typed pointers into a plan buffer; the second form takes the plan kernels'
+// scratch (the layout's [persist_bytes, bytes)) from scratch_base instead.
 PlanPtrs resolve(const moonep_layout &lay, void *base);
+PlanPtrs resolve(const moonep_layout &lay, void *base, void *scratch_base);
 
 // While non-null on the calling thread, the chunked move launchers (dispatch,
 // combine) add their launches to it and enqueue nothing.
