@@ -126,6 +126,61 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, co
     return rec
 
 
+# Kernel classes of a counter summary: the library's kernels and the streaming
+# kernels the ceilings are measured with.
+PMC_CLASSES = ("k_count", "k_scan", "k_solve", "k_assign", "k_replicate", "k_dispatch",
+               "k_combine", "k_reduce", "k_bwd_dot", "k_bwd_scatter", "k_stream_read",
+               "k_stream_write", "k_stream_copy")
+
+
+def pmc_summary(dirs):
+    """Per kernel class, from rocprofv3 runs that each wrote a *counter_collection.csv
+    (--pmc) and a *kernel_trace.csv (--kernel-trace) into one of `dirs`: dispatches,
+    median duration, the mean of every counter per dispatch and, where the counters
+    are there, EA request sizes, latencies (LEVEL / requests, in cycles) and
+    requests in flight (LEVEL / GRBM_GUI_ACTIVE x 8: GRBM_GUI_ACTIVE counts the
+    cycles of all 8 XCDs)."""
+    import csv
+    import glob
+
+    def cls(name):
+        return next((c for c in PMC_CLASSES if c + "<" in name or c + "(" in name), None)
+
+    out = {}
+    for d in dirs:
+        rec = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            sums, disp = {}, {}
+            for r in csv.DictReader(open(f)):
+                c = cls(r["Kernel_Name"])
+                if c is None:
+                    continue
+                sums.setdefault(c, {}).setdefault(r["Counter_Name"], 0.0)
+                sums[c][r["Counter_Name"]] += float(r["Counter_Value"])
+                disp.setdefault(c, set()).add(r["Dispatch_Id"])
+            for c, kv in sums.items():
+                rec.setdefault(c, {})["dispatches"] = len(disp[c])
+                rec[c].update({k: v / len(disp[c]) for k, v in kv.items()})
+        for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            durs = {}
+            for r in csv.DictReader(open(f)):
+                c = cls(r["Kernel_Name"])
+                if c is not None:
+                    durs.setdefault(c, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            for c, v in durs.items():
+                v.sort()
+                rec.setdefault(c, {})["median_us"] = v[len(v) // 2] / 1e3
+        for c, k in rec.items():
+            for side in ("RDREQ", "WRREQ"):
+                n, lvl = k.get(f"TCC_EA0_{side}_sum"), k.get(f"TCC_EA0_{side}_LEVEL_sum")
+                if n and lvl is not None:
+                    k[f"{side.lower()}_latency_cycles"] = lvl / n
+                    if k.get("GRBM_GUI_ACTIVE"):
+                        k[f"{side.lower()}_in_flight"] = lvl / k["GRBM_GUI_ACTIVE"] * 8
+        out[os.path.basename(os.path.normpath(d))] = rec
+    return out
+
+
 def plan_latency(plan_fn, dims, ids_d, plan_buf, stream, iters):
     """The plan call alone, timed with events on its stream: warm (the ids were
     just written by a device copy, as a router would leave them) and cold (after
@@ -197,67 +252,159 @@ def host_cpu() -> str:
     return f"{model}, {os.cpu_count()} logical CPUs"
 
 
-def cpu_baseline(wl, ids, w, hidden_dev, y_dev, budget_s):
-    """The oracle as it stands, single thread, on a bounded sample of the workload:
-    the full plan; dispatch of whole destination-rank windows (the oracle streams
-    its output by rank) for about half the budget; combine of the first n tokens
-    for the rest. Times are scaled to the whole workload (R windows; all tokens)."""
+def host_threads() -> int:
+    """Threads this process may run on: OMP_NUM_THREADS if set, else the CPUs it
+    is allowed on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, ids, w, hidden_dev, budget_s):
+    """The oracle as it stands, on the host's cores, on a bounded sample of the
+    workload: the plan (sequential by nature, one thread); dispatch into a host
+    receive buffer; combine of consecutive token batches that read their K rows
+    from that buffer inside the timed call (identity expert, y = recv, as on the
+    GPU). Dispatch and combine run once with the oracle's OpenMP loops on every
+    thread the process may use and once on one thread. The receive buffer is
+    allocated and its pages touched by an untimed dispatch first, as a CPU
+    implementation would keep it between steps. Times are scaled to the whole
+    workload (all slots, all tokens)."""
     import numpy as np
     import torch
     import oracle
     import workloads as W
 
+    threads = host_threads()
     t0 = time.perf_counter()
     p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
     t_plan = time.perf_counter() - t0
 
-    hid = hidden_dev.view(wl.n_tok, wl.H).cpu().view(torch.int16).numpy().view(np.uint16)
-    t_disp, ranks = 0.0, 0
-    while ranks < wl.R and (ranks == 0 or t_disp < 0.5 * budget_s):
-        t0 = time.perf_counter()
-        oracle.dispatch(p, wl.K, hid, ranks * wl.SK, (ranks + 1) * wl.SK)
-        t_disp += time.perf_counter() - t0
-        ranks += 1
-    del hid
-
-    def gather(t0, n):
-        dsel = p["dst"][t0 * wl.K:(t0 + n) * wl.K].astype(np.int64)
-        rows = y_dev.view(-1, wl.H)[torch.from_numpy(dsel).to(y_dev.device)].cpu()
-        if wl.dtype == W.BF16:
-            return rows.view(torch.int16).numpy().view(np.uint16)
-        return rows.numpy()
-
-    def comb(t0, n, y_rows):
-        t0w = time.perf_counter()
-        oracle.combine(np.arange(n * wl.K, dtype=np.int32), wl.K, y_rows,
-                       w.reshape(-1)[t0 * wl.K:(t0 + n) * wl.K], wl.dtype, wl.dtype)
-        return time.perf_counter() - t0w
-
-    # consecutive batches of at most 8192 tokens (bounded host memory for the
-    # gathered rows) until the rest of the budget is spent or every token is done
-    left = max(0.0, budget_s - t_plan - t_disp)
-    t_comb, n = 0.0, 0
-    while n < wl.n_tok and (n == 0 or t_comb < left):
-        m = min(8192, wl.n_tok - n)
-        rows = gather(n, m)
-        t_comb += comb(n, m, rows)
-        n += m
-        del rows
-
+    hid = hidden_dev.view(wl.n_tok, wl.H).cpu()
+    hid = hid.view(torch.int16).numpy().view(np.uint16) if wl.dtype == W.BF16 else hid.numpy()
+    recv = np.empty((wl.n_ent, wl.H), dtype=hid.dtype)
+    wf = w.reshape(-1)
+    dt = W.BF16 if wl.dtype == W.BF16 else W.F32
     nbytes = algorithmic_bytes(wl, 0, 0)
-    t_d_full = t_disp / ranks * wl.R
-    t_c_full = t_comb * wl.n_tok / n
-    gbs = (nbytes["dispatch"] + nbytes["combine"]) / (t_d_full + t_c_full) / 1e9
+    oracle.set_threads(threads)
+    oracle.dispatch(p, wl.K, hid, out=recv)  # untimed: touches every page of recv
+
+    def run(n_threads, budget):
+        """(seconds of dispatch scaled to all slots, of combine scaled to all
+        tokens, what was sampled) on n_threads threads within about `budget` s."""
+        oracle.set_threads(n_threads)
+        # dispatch: whole destination-rank windows until half the budget is spent
+        t_d, ranks = 0.0, 0
+        while ranks < wl.R and (ranks == 0 or t_d < 0.5 * budget):
+            step = wl.R if n_threads > 1 and ranks == 0 else 1  # all windows in one call
+            lo, hi = ranks * wl.SK, (ranks + step) * wl.SK
+            t0 = time.perf_counter()
+            oracle.dispatch(p, wl.K, hid, lo, hi, out=recv[lo:hi])
+            t_d += time.perf_counter() - t0
+            ranks += step
+        # combine: batches of at most 8192 tokens until the rest of the budget is spent
+        out = np.empty((8192, wl.H), dtype=hid.dtype)
+        t_c, n = 0.0, 0
+        while n < wl.n_tok and (n == 0 or t_c < budget - t_d):
+            m = min(8192, wl.n_tok - n)
+            t0 = time.perf_counter()
+            res = oracle.combine(p["dst"][n * wl.K:(n + m) * wl.K], wl.K, recv,
+                                 wf[n * wl.K:(n + m) * wl.K], dt, dt)
+            t_c += time.perf_counter() - t0
+            out[:m] = res
+            n += m
+        sample = (f"dispatch of {ranks} of {wl.R} destination-rank windows ({t_d:.2f} s, "
+                  f"scaled x{wl.R / ranks:.2f}); combine of {n} of {wl.n_tok} tokens "
+                  f"({t_c:.2f} s, scaled x{wl.n_tok / n:.2f})")
+        return t_d / ranks * wl.R, t_c * wl.n_tok / n, t_d + t_c, sample
+
+    d_n, c_n, meas_n, sample_n = run(threads, 0.6 * budget_s)
+    d_1, c_1, meas_1, sample_1 = run(1, 0.4 * budget_s)
+    oracle.set_threads(threads)
+    dc = nbytes["dispatch"] + nbytes["combine"]
+    gbs_n = dc / (d_n + c_n) / 1e9
+    gbs_1 = dc / (d_1 + c_1) / 1e9
+    del recv, hid
     return {
-        "value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"full plan of {wl.n_ent} entries ({t_plan * 1e3:.1f} ms); dispatch of "
-                   f"{ranks} of {wl.R} destination-rank windows ({t_disp:.2f} s, scaled x"
-                   f"{wl.R / ranks:.2f}); combine of {n} of {wl.n_tok} tokens ({t_comb:.2f} s, "
-                   f"scaled x{wl.n_tok / n:.1f})"),
+        "value": round(gbs_n, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"full plan of {wl.n_ent} entries, one thread ({t_plan * 1e3:.1f} ms); on "
+                   f"{threads} threads: {sample_n}; combine reads its rows from the host "
+                   f"receive buffer inside the timed call"),
+        "ms": {"dispatch": round(d_n * 1e3, 1), "combine": round(c_n * 1e3, 1)},
+        "one_thread": {"value": round(gbs_1, 3), "unit": "GB/s", "sample": sample_1,
+                       "ms": {"dispatch": round(d_1 * 1e3, 1), "combine": round(c_1 * 1e3, 1)}},
         "plan_us": round(t_plan * 1e6, 1),
-        "measured_s": round(t_plan + t_disp + t_comb, 2),
+        "measured_s": round(t_plan + meas_n + meas_1, 2),
         "host": host_cpu(),
     }
+
+
+def ceilings(wl, buf, stream, reps):
+    """Practical HBM ceilings on the receive buffer itself (the 30 GB that
+    dispatch writes and combine reads at K3): plain sequential reads, writes and
+    copies (first half into second half) with this library's streaming kernels in
+    both launch shapes (one resident grid; one workgroup per 16 KiB), and torch's
+    fill_ (the runtime's memset kernel) and copy_. GB/s of bytes moved (read +
+    written), median of `reps` after one warm-up. `read`, `write` and `copy` are
+    the best of each kind. The receive buffer is overwritten."""
+    import numpy as np
+    import torch
+    from token_dispatch_amd import stream as ts
+
+    flat = buf.view(-1).view(torch.uint8)
+    n = flat.numel() // 32 * 32
+    half = n // 2
+    a, b = flat[:half], flat[half:2 * half]
+    sink = torch.zeros(16, dtype=torch.uint8, device=buf.device)
+
+    def timed(fn, nbytes):
+        ms = []
+        for i in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            if i:
+                ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms))
+        return round(nbytes / (t * 1e-3) / 1e9, 1)
+
+    chunk = 16384
+    runs = {
+        "read_grid": timed(lambda: ts.stream_read(flat[:n], sink, 0, stream), n),
+        "read_16k": timed(lambda: ts.stream_read(flat[:n], sink, chunk, stream), n),
+        "write_grid": timed(lambda: ts.stream_write(flat[:n], 0, 0, stream), n),
+        "write_16k": timed(lambda: ts.stream_write(flat[:n], 0, chunk, stream), n),
+        "torch_fill": timed(lambda: flat[:n].fill_(0), n),
+        "copy_grid": timed(lambda: ts.stream_copy(b, a, 0, stream), 2 * half),
+        "copy_16k": timed(lambda: ts.stream_copy(b, a, chunk, stream), 2 * half),
+        "torch_copy": timed(lambda: b.copy_(a), 2 * half),
+    }
+    out = {kind: max(v for k, v in runs.items() if kind in k) for kind in ("read", "write", "copy")}
+    out["write"] = max(out["write"], runs["torch_fill"])
+    out.update({"runs": runs, "bytes": n, "unit": "GB/s", "reps": reps,
+                "kernels": "moonep_stream_read / _write / _copy (include/moonep_stream.h): 16-byte "
+                           "accesses, non-temporal loads; torch_fill = fill_(0), torch_copy = copy_"})
+    return out
+
+
+def ceiling_time_s(rd, wr, c):
+    """Seconds a move of rd bytes read and wr bytes written takes at the measured
+    pure-read and pure-write rates (no cost for mixing the two)."""
+    return rd / (c["read"] * 1e9) + wr / (c["write"] * 1e9)
+
+
+def move_directions(wl):
+    """(bytes read, bytes written) of dispatch and combine, algorithmic."""
+    row = wl.row_bytes
+    return {"dispatch": (wl.n_tok * row + 4 * wl.n_ent, wl.n_ent * row),
+            "combine": (wl.n_ent * row + 8 * wl.n_ent, wl.n_tok * row)}
 
 
 def main():
@@ -274,6 +421,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain read / write / copy streams over the receive buffer "
+                         "(the practical ceilings the moves are compared with)")
+    ap.add_argument("--ceiling-reps", type=int, default=5)
+    ap.add_argument("--alloc-order", default="model-first",
+                    choices=["model-first", "activations-first"],
+                    help="allocate the model state (weights, duplicate slots, gradients) before "
+                         "the step's activations (hidden, receive buffer), as a training process "
+                         "does, or after them; where the 30 GB receive buffer lands in physical "
+                         "memory depends on it, and dispatch's speed on that")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (graph_ms_per_step)")
     ap.add_argument("--with-backward", action="store_true",
@@ -288,9 +445,16 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs "
                          "of a run with --copy-calibration (same --steps/--warmup), then exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="print a per-kernel summary of rocprofv3 --pmc / --kernel-trace CSVs "
+                         "found under each DIR (one JSON object per DIR), then exit")
     ap.add_argument("--traffic-command", default="",
                     help="the profiled command, recorded in the traffic summary")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary), indent=1, sort_keys=True))
+        return
 
     if args.traffic_from:
         rec = traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.steps,
@@ -319,15 +483,22 @@ def main():
           file=sys.stderr, flush=True)
     ids, w = W.make_routing(wl, args.seed)
     dims = td.Dims(wl.R, wl.E, wl.K, wl.S, wl.B, wl.dtype, wl.H)
-    # model state first (expert weights, duplicate slots, gradients), then the
-    # step's activations, in the order a training process allocates them
-    expert_w = W.make_expert_weights(wl, args.seed, dev)
-    dup_w = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=expert_w.dtype, device=dev)
-    dup_g, home_g = W.make_grads(wl, args.seed, dev)
-    ids_d = torch.from_numpy(ids).to(dev)
-    w_d = torch.from_numpy(w).to(dev)
+    # by default the model state first (expert weights, duplicate slots,
+    # gradients), then the step's activations, in the order a training process
+    # allocates them; --alloc-order activations-first reverses that
+    def model_state():
+        ew = W.make_expert_weights(wl, args.seed, dev)
+        dw = torch.empty((wl.R, wl.B) + tuple(wl.block_shape), dtype=ew.dtype, device=dev)
+        return (ew, dw) + tuple(W.make_grads(wl, args.seed, dev))
+
+    if args.alloc_order == "model-first":
+        expert_w, dup_w, dup_g, home_g = model_state()
     hidden = W.make_hidden(wl, args.seed, dev)
     recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hidden.dtype, device=dev)
+    if args.alloc_order == "activations-first":
+        expert_w, dup_w, dup_g, home_g = model_state()
+    ids_d = torch.from_numpy(ids).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
     out = torch.empty_like(hidden)
     plan_buf = td.new_plan_buffer(dims, dev)
     if args.with_backward:
@@ -395,6 +566,10 @@ def main():
     if args.plan_iters > 0 and not args.copy_calibration:
         plan_lat = plan_latency(plan_fn, dims, ids_d, plan_buf, stream, args.plan_iters)
         print(f"# plan latency: {plan_lat}", file=sys.stderr, flush=True)
+    ceil = None
+    if not args.no_ceiling and not args.copy_calibration:
+        ceil = ceilings(wl, recv, stream, args.ceiling_reps)
+        print(f"# ceilings: {ceil}", file=sys.stderr, flush=True)
     if args.copy_calibration:
         a = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -440,10 +615,24 @@ def main():
                 "launch": f"moonep_{dom} enqueues {n_launch} launches of k_{dom} over token "
                           "chunks; per-launch figures are the call's over that count"}
 
+    if ceil is not None:
+        # each move against the time its read and written bytes take at the pure
+        # read and write rates of the same buffer (direction mixing not charged)
+        dirs = move_directions(wl)
+        t_dc = 0.0
+        fr = {}
+        for op in ("dispatch", "combine"):
+            t = ceiling_time_s(*dirs[op], ceil)
+            t_dc += t
+            fr[op] = round(t / (op_ms[op] * 1e-3), 4)
+        ceil["dispatch_combine_gbs"] = round(dc_bytes / t_dc / 1e9, 1)
+        ceil["frac_of_ceiling"] = dict(fr, dispatch_combine=round(value / (dc_bytes / t_dc / 1e9), 4))
+        ceil["frac_of_peak"] = {op: round(gbs[op] / HBM_PEAK_GBS, 4) for op in ops}
+        roofline["frac_of_ceiling"] = fr[dom]
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, ids, w, hidden, recv, args.cpu_budget)
+        cpu = cpu_baseline(wl, ids, w, hidden, args.cpu_budget)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -454,6 +643,7 @@ def main():
                                f"S={wl.S}, H={wl.H}, B={wl.B}, weight block "
                                f"{'x'.join(map(str, wl.block_shape))}",
                    "routing": wl.routing, "seed": args.seed, "plan": args.plan,
+                   "alloc_order": args.alloc_order,
                    "parallelism": "ep (virtual, 1 GPU)"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "plan_us": round(op_ms["plan"] * 1e3, 2), "plan_latency_us": plan_lat,
@@ -464,7 +654,7 @@ def main():
         "dups_per_rank_max": int(n_dup.max()), "dups_total": int(n_dup.sum()), "B": wl.B,
         "dups_materialised": n_mat, "experts_with_dups": n_xm,
         "status": status, "kernel_source_hash": src_hash,
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "ceiling": ceil, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

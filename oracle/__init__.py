@@ -3,8 +3,10 @@
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg load it; the HIP library never does, and the two share no code.
 The arithmetic lives in moonep_oracle.c (plain loops, built with gcc
--O2 -ffp-contract=off); this module builds it on first use and marshals numpy
-arrays in and out. Each function names the passage it follows in its C source.
+-O2 -ffp-contract=off -fopenmp; the data moves spread their outer loop over
+threads, every output element with one writer, so the thread count never changes
+a bit); this module builds it on first use and marshals numpy arrays in and out.
+Each function names the passage it follows in its C source.
 
 Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   plan      -- pinned: library histogram, hand-worked examples, an independent
@@ -44,12 +46,16 @@ BF16 = 1
 ST_BAD_ID, ST_REPEAT_ID, ST_OVER_B = 1, 2, 4
 
 
+# gcc flags of the oracle (plain C, no contraction of a*b+c; OpenMP for the moves)
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+          "-fPIC"]
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain C, no contraction of a*b+c)."""
+    """Compile the oracle with gcc."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-                               "-shared", "-fPIC", "-Wall", "-Werror", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc"] + CFLAGS + ["-Wall", "-Werror", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -104,6 +110,10 @@ def _load() -> ctypes.CDLL:
         lib.oracle_combine_backward_w.restype = None
         lib.oracle_dispatch_backward.argtypes = [i64, i32, i64, i32, i32, vp, vp, vp]
         lib.oracle_dispatch_backward.restype = None
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_set_threads.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
         _lib = lib
     return _lib
 
@@ -160,9 +170,21 @@ def plan(R: int, E: int, K: int, S: int, B: int, ids: np.ndarray,
     return out
 
 
+def set_threads(n: int) -> None:
+    """Threads of the data moves (the plan always runs on one)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
 def dispatch(plan_out: Dict[str, np.ndarray], K: int, hidden: np.ndarray,
-             slot_lo: int = 0, slot_hi: Optional[int] = None) -> np.ndarray:
-    """recv rows for slots [slot_lo, slot_hi): bytes of hidden [n_tok, H] (any dtype)."""
+             slot_lo: int = 0, slot_hi: Optional[int] = None,
+             out: Optional[np.ndarray] = None) -> np.ndarray:
+    """recv rows for slots [slot_lo, slot_hi): bytes of hidden [n_tok, H] (any dtype).
+    `out`, if given, receives them (rows of slots holding no entry keep its contents);
+    else a zeroed array is returned."""
     lib = _load()
     hidden = np.ascontiguousarray(hidden)
     n_tok = hidden.shape[0]
@@ -170,7 +192,13 @@ def dispatch(plan_out: Dict[str, np.ndarray], K: int, hidden: np.ndarray,
     dst = plan_out["dst"]
     if slot_hi is None:
         slot_hi = dst.size
-    recv = np.zeros((slot_hi - slot_lo,) + hidden.shape[1:], dtype=hidden.dtype)
+    shape = (slot_hi - slot_lo,) + hidden.shape[1:]
+    if out is None:
+        recv = np.zeros(shape, dtype=hidden.dtype)
+    else:
+        if out.shape != shape or out.dtype != hidden.dtype or not out.flags["C_CONTIGUOUS"]:
+            raise ValueError("out must be a contiguous array of the window's shape and dtype")
+        recv = out
     lib.oracle_dispatch(dst.size, K, row_bytes, _ptr(hidden), _ptr(dst), slot_lo, slot_hi,
                         _ptr(recv))
     assert n_tok * K == dst.size

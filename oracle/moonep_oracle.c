@@ -29,8 +29,13 @@
  * in ascending k from +0.0f and rounds the accumulator to nearest-even bf16;
  * the gradient reduce adds in binary32, home value first, then duplicates in
  * ascending rank. Build with -ffp-contract=off so that no other fusion happens.
+ *
+ * The data moves spread their outer loop over threads with OpenMP (built with
+ * -fopenmp); each output element has one writer and its own fixed order of
+ * operations, so any thread count gives the same bits as one thread.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -221,6 +226,7 @@ int oracle_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
 void oracle_dispatch(int64_t n_ent, int32_t K, int64_t row_bytes, const uint8_t *hidden,
                      const int32_t *dst, int64_t slot_lo, int64_t slot_hi, uint8_t *recv_window)
 {
+    #pragma omp parallel for schedule(static)
     for (int64_t a = 0; a < n_ent; ++a) {
         int64_t d = dst[a];
         if (d < slot_lo || d >= slot_hi) continue;
@@ -234,6 +240,7 @@ void oracle_replicate(int32_t R, int32_t B, int32_t dcap, const int32_t *n_dup,
                       const int32_t *dup_expert, int64_t block_bytes,
                       const uint8_t *expert_w, uint8_t *dup_w)
 {
+    #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < R; ++r)
         for (int b = 0; b < n_dup[r] && b < B; ++b)
             memcpy(dup_w + ((int64_t)r * B + b) * block_bytes,
@@ -267,6 +274,7 @@ static uint16_t f32_to_bf16_rne(float f)
 void oracle_combine(int64_t n_tok, int32_t K, int64_t H, int32_t in_dtype, int32_t out_dtype,
                     const void *y, const int32_t *dst, const float *w, void *out)
 {
+    #pragma omp parallel for schedule(static)
     for (int64_t g = 0; g < n_tok; ++g)
         for (int64_t i = 0; i < H; ++i) {
             float acc = 0.0f;
@@ -291,6 +299,7 @@ void oracle_reduce(int32_t E, int32_t B, int64_t n, const int32_t *dup_ptr,
                    const int32_t *list_rank, const int32_t *list_b,
                    const float *dup_grads, float *home)
 {
+    #pragma omp parallel for collapse(2) schedule(static)
     for (int e = 0; e < E; ++e)
         for (int64_t i = 0; i < n; ++i) {
             float v = home[(int64_t)e * n + i];
@@ -301,6 +310,13 @@ void oracle_reduce(int32_t E, int32_t B, int64_t n, const int32_t *dup_ptr,
             home[(int64_t)e * n + i] = v;
         }
 }
+
+/* Threads of the data moves and their backward (the plan is one thread: its
+   prefix sums and running counters are sequential). Every output element of a
+   move has exactly one writer -- a slot holds one entry, a token row, an expert
+   element -- so the results do not depend on the number of threads. */
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+int32_t oracle_max_threads(void) { return (int32_t)omp_get_max_threads(); }
 
 /* The rounding used by combine, exposed so tests can pin it to a library. */
 void oracle_f32_to_bf16(int64_t n, const float *x, uint16_t *y)
@@ -339,6 +355,7 @@ void oracle_combine_backward_y(int64_t n_ent, int32_t K, int64_t H, int32_t gout
                                const int32_t *dst, int64_t slot_lo, int64_t slot_hi,
                                void *grad_y_window)
 {
+    #pragma omp parallel for schedule(static)
     for (int64_t a = 0; a < n_ent; ++a) {
         int64_t d = dst[a];
         if (d < slot_lo || d >= slot_hi) continue;
@@ -358,6 +375,7 @@ void oracle_combine_backward_w(int64_t n_tok, int32_t K, int64_t H, int32_t gout
                                int32_t y_dtype, const void *grad_out, const void *y_rows,
                                const int32_t *dst, double *grad_w)
 {
+    #pragma omp parallel for schedule(static)
     for (int64_t g = 0; g < n_tok; ++g)
         for (int k = 0; k < K; ++k) {
             int64_t a = g * K + k;
@@ -376,6 +394,7 @@ void oracle_dispatch_backward(int64_t n_tok, int32_t K, int64_t H, int32_t in_dt
                               int32_t out_dtype, const void *grad_recv, const int32_t *dst,
                               void *grad_hidden)
 {
+    #pragma omp parallel for schedule(static)
     for (int64_t g = 0; g < n_tok; ++g)
         for (int64_t i = 0; i < H; ++i) {
             float acc = 0.0f;

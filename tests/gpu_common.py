@@ -61,3 +61,37 @@ def bf16_bits(t):
 
 def f32_bits(t):
     return t.detach().contiguous().cpu().numpy().view(np.uint32)
+
+
+class HostStage:
+    """A pinned host buffer through which device tensors are copied to the host in
+    batches; fetch() returns a numpy view that is valid until the next fetch."""
+
+    def __init__(self, nbytes: int):
+        import torch
+        self.buf = torch.empty(max(16, int(nbytes)), dtype=torch.uint8, pin_memory=True)
+
+    def fetch(self, t):
+        import torch
+        t = t.contiguous()
+        n = t.numel() * t.element_size()
+        assert n <= self.buf.numel(), f"stage of {self.buf.numel()} bytes, needs {n}"
+        h = self.buf[:n].view(t.dtype).view(t.shape)
+        h.copy_(t)
+        if t.dtype == torch.bfloat16:
+            return h.view(torch.int16).numpy().view(np.uint16)
+        return h.numpy()
+
+
+def token_batches(n_tok: int, K: int, row_bytes: int, budget: int = 1 << 30):
+    """Token ranges [t0, t0 + n) whose K gathered rows take at most `budget` bytes."""
+    tb = max(1, min(n_tok, budget // (K * row_bytes)))
+    for t0 in range(0, n_tok, tb):
+        yield t0, min(tb, n_tok - t0)
+
+
+def local_dst(dst_tokens: np.ndarray) -> np.ndarray:
+    """Entry a of a batch reads gathered row a; dropped entries stay -1."""
+    d = np.arange(dst_tokens.size, dtype=np.int32)
+    d[dst_tokens.reshape(-1) < 0] = -1
+    return d

@@ -21,8 +21,8 @@ def td():
     return td
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moonep_[a-z_]+)\s*\(", text)))
 
@@ -33,6 +33,26 @@ def test_exports_every_declared_function(td):
     lib = ctypes.CDLL(td.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_stream_library_exports_its_header():
+    """libmoonep_stream.so (the ceiling kernels) exports what moonep_stream.h declares,
+    and every header under include/ belongs to one of the two libraries."""
+    from token_dispatch_amd import stream
+    headers = sorted(os.listdir(os.path.join(ROOT, "include")))
+    assert headers == ["moonep.h", "moonep_stream.h"]
+    names = _declared_functions(os.path.join(ROOT, "include", "moonep_stream.h"))
+    assert set(names) == set(stream.ENTRY_POINTS)
+    lib = ctypes.CDLL(stream.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    ok = ctypes.c_void_p(1 << 20)
+    i64 = ctypes.c_int64
+    assert stream._lib.moonep_stream_read(ok, 24, 0, ok, None) == -1
+    assert stream._lib.moonep_stream_read(ok, 0, 0, ok, None) == -1
+    assert stream._lib.moonep_stream_read(ok, 1 << 20, 1000, ok, None) == -1
+    assert stream._lib.moonep_stream_write(ctypes.c_void_p((1 << 20) + 8), 32, 0, 0, None) == -2
+    assert stream._lib.moonep_stream_copy(None, ok, 32, 4096, None) == -2
 
 
 def _dims(td, R=32, E=896, K=16, S=4096, B=28, dtype=1, H=7168):

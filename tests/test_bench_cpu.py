@@ -109,7 +109,57 @@ def test_cpu_baseline_runs_on_host_tensors(name, dt):
         wl = wl.replace(dtype=dt)
     ids, w = W.make_routing(wl, 0)
     hidden = W.make_hidden(wl, 0)
-    recv = torch.zeros((wl.R, wl.SK, wl.H), dtype=hidden.dtype)
-    rec = bench.cpu_baseline(wl, ids, w, hidden, recv, 0.2)
-    assert rec["value"] > 0 and rec["cores"] == 1 and rec["kind"] == "oracle"
-    assert "destination-rank windows" in rec["sample"]
+    rec = bench.cpu_baseline(wl, ids, w, hidden, 0.2)
+    assert rec["value"] > 0 and rec["kind"] == "oracle"
+    assert rec["cores"] == bench.host_threads() >= 1
+    assert rec["one_thread"]["value"] > 0
+    assert "destination-rank windows" in rec["sample"] and "tokens" in rec["one_thread"]["sample"]
+    assert set(rec["ms"]) == {"dispatch", "combine"}
+
+
+def test_host_threads_follows_omp_num_threads(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.host_threads() == 3
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_threads() == len(os.sched_getaffinity(0))
+
+
+def test_ceiling_fractions_by_hand():
+    """A move that takes exactly its read bytes at the read rate plus its written
+    bytes at the write rate is at the ceiling."""
+    wl = W.WORKLOADS["k3"]
+    c = {"read": 7000.0, "write": 6800.0}
+    dirs = bench.move_directions(wl)
+    rd, wr = dirs["dispatch"]
+    assert rd + wr == bench.algorithmic_bytes(wl, 0, 0)["dispatch"]
+    assert bench.ceiling_time_s(rd, wr, c) == pytest.approx(rd / 7.0e12 + wr / 6.8e12)
+    rd, wr = dirs["combine"]
+    assert rd + wr == bench.algorithmic_bytes(wl, 0, 0)["combine"]
+
+
+def test_pmc_summary_by_hand(tmp_path):
+    """Counters are averaged per dispatch and per kernel class; latency is LEVEL
+    over requests, requests in flight LEVEL over GRBM_GUI_ACTIVE times 8."""
+    import csv as _csv
+    d = tmp_path / "run"
+    d.mkdir()
+    name = "void moonep::(anonymous namespace)::k_combine<14, true, true, false>(int)"
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for did in (1, 2):
+            w.writerow([did, name, "TCC_EA0_RDREQ_sum", 100.0])
+            w.writerow([did, name, "TCC_EA0_RDREQ_LEVEL_sum", 5000.0 * did])
+            w.writerow([did, name, "GRBM_GUI_ACTIVE", 800.0])
+        w.writerow([3, "other_kernel(int)", "TCC_EA0_RDREQ_sum", 1.0])
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerow([name, 0, 1000])
+        w.writerow([name, 0, 3000])
+        w.writerow([name, 0, 2000])
+    rec = bench.pmc_summary([str(d)])["run"]["k_combine"]
+    assert rec["dispatches"] == 2 and rec["TCC_EA0_RDREQ_sum"] == 100.0
+    assert rec["rdreq_latency_cycles"] == pytest.approx(75.0)
+    assert rec["rdreq_in_flight"] == pytest.approx(7500.0 / 800.0 * 8)
+    assert rec["median_us"] == pytest.approx(2.0)

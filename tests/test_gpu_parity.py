@@ -11,9 +11,10 @@ duplicates per rank (moonep_plan_bounded), each against its oracle.
 Small shapes are compared element by element; they span several plan tiles with
 a ragged last tile and rows whose 16-byte chunk count does not fill the lanes.
 The five workload shapes are run at full size in the launch configuration the
-benchmark times: the whole plan is compared, dispatch and replicate are checked
-everywhere against the oracle's plan tables, combine and reduce on sampled
-tokens / experts that the oracle computes one by one.
+benchmark times, for seeds 0, 1 and 2: the whole plan is compared, dispatch and
+replicate are checked everywhere against the oracle's plan tables, combine on
+every token and reduce on every expert with duplicates through the oracle
+(batches of rows streamed to the host), the other experts checked untouched.
 """
 import numpy as np
 import pytest
@@ -21,8 +22,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_common import (PLAN_INT_KEYS, assert_plan_equal, bf16_bits, f32_bits, read_plan,
-                              run_plan, say)
+from tests.gpu_common import (PLAN_INT_KEYS, HostStage, assert_plan_equal, bf16_bits, f32_bits,
+                              local_dst, read_plan, run_plan, say, token_batches)
 from tests.invariants import check_plan
 
 pytestmark = pytest.mark.gpu
@@ -557,8 +558,8 @@ def test_entries_near_int32_limit(td):
     """The largest entry count the library takes: R*S*K = 2 147 483 520, just
     below 2^31 (16 ranks, 64 experts, K = 8, 16 777 215 tokens per rank, 16-byte
     rows). Both plans are compared with the oracle array by array; dispatch on
-    200 000 sampled slots; combine with identity experts and weights 1/K, whose
-    exact result is the token's own row, on 200 000 sampled tokens."""
+    every slot against the oracle's inverse map; combine with identity experts and
+    weights 1/K, whose exact result is the token's own row, on every token."""
     R, E, K, B, H = 16, 64, 8, 4, 8
     S = ((1 << 31) - 1) // (R * K)
     n_ent, n_tok = R * S * K, R * S
@@ -581,18 +582,22 @@ def test_entries_near_int32_limit(td):
     td.moonep_combine(dims, plan_buf, recv, w_d, out)
     torch.cuda.synchronize()
     say("dispatch and combine done")
-    rng = np.random.default_rng(3)
-    slots = rng.integers(0, n_ent, 200_000)
-    slots[:2] = (0, n_ent - 1)
-    tok_of_slot = (p["src"][slots].astype(np.int64)) // K
-    got = recv.view(-1, H)[torch.from_numpy(slots).to(DEV)]
-    want = hidden.view(-1, H)[torch.from_numpy(tok_of_slot).to(DEV)]
-    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "dispatch"
-    toks = rng.integers(0, n_tok, 200_000)
-    toks[:2] = (0, n_tok - 1)
-    tk = torch.from_numpy(toks).to(DEV)
-    assert torch.equal(out.view(-1, H)[tk].view(torch.int16),
-                       hidden.view(-1, H)[tk].view(torch.int16)), "combine"
+    # dispatch: every slot against the oracle's inverse map, 2^24 slots at a time
+    # (torch's own kernels refuse a launch over 2^30 elements)
+    step = 1 << 24
+    hflat, rflat = hidden.view(-1, H), recv.view(-1, H)
+    for lo in range(0, n_ent, step):
+        hi = min(n_ent, lo + step)
+        tok = torch.from_numpy(p["src"][lo:hi].astype(np.int64) // K).to(DEV)
+        assert torch.equal(rflat[lo:hi].view(torch.int16), hflat[tok].view(torch.int16)), \
+            f"dispatch slots [{lo}, {hi})"
+        del tok
+    # combine: identity experts and weights 1/K give every token its own row back
+    oflat = out.view(-1, H)
+    for lo in range(0, n_tok, step):
+        assert torch.equal(oflat[lo:lo + step].view(torch.int16),
+                           hflat[lo:lo + step].view(torch.int16)), f"combine tokens from {lo}"
+    say("every slot and every token equal")
     del recv, out, w_d, hidden
 
     td.moonep_plan_bounded(dims, ids_d, plan_buf)
@@ -628,19 +633,39 @@ def test_workload_plans_all_seeds(td, name, bounded):
             f"(B={wl.B})  total dups {int(g['n_dup'].sum())}  status {int(g['status'][0])}")
 
 
-@pytest.mark.parametrize("name,bounded", [("uniform", False), ("zipf", False), ("k3", False),
-                                          ("decode", False), ("k3", True), ("decode", True)])
-def test_workload_data_moves_full_size(td, name, bounded):
+FULL_MOVES = [("uniform", False), ("zipf", False), ("k3", False), ("decode", False),
+              ("k3", True), ("decode", True)]
+
+
+def _row_hash(t, rows_per_chunk=8):
+    """One int64 per row of a float32 [n, m] tensor: the sum of its bit patterns
+    (any write that changes a row changes it with overwhelming probability),
+    taken a few rows at a time to bound the temporary."""
+    out = torch.empty(t.shape[0], dtype=torch.int64, device=t.device)
+    for i in range(0, t.shape[0], rows_per_chunk):
+        out[i:i + rows_per_chunk] = t[i:i + rows_per_chunk].view(torch.int32).to(torch.int64).sum(1)
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name,bounded", FULL_MOVES, ids=[f"{n}-{'bounded' if b else 'waterfill'}"
+                                                          for n, b in FULL_MOVES])
+def test_workload_data_moves_full_size(td, name, bounded, seed):
+    """Every output element of dispatch, combine, replicate and reduce at the
+    workload's full size, in the launch configuration the benchmark times, against
+    the oracle: dispatch and replicate through the oracle's plan tables, combine
+    through the oracle's fma sequence on every token (batches of gathered rows),
+    reduce through the oracle on every expert with duplicates, and the experts
+    without any checked untouched."""
     wl = W.WORKLOADS[name]
     dims = _dims(td, wl)
-    seed = 0
-    say(f"full-size moves {name} bounded={bounded}: {dims}")
+    say(f"full-size moves {name} bounded={bounded} seed={seed}: {dims}")
     ids, w = W.make_routing(wl, seed)
     p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
     pb, _ = run_plan(td, dims, ids, DEV, bounded=bounded)
     assert_plan_equal(read_plan(td, dims, pb), p)
     src_d = torch.from_numpy(p["src"].astype(np.int64)).to(DEV)
-    rng = np.random.default_rng(99)
+    rng = np.random.default_rng(99 + seed)
 
     # dispatch: every slot against the oracle's inverse map, windows through the oracle
     hid = W.make_hidden(wl, seed, DEV)
@@ -649,6 +674,7 @@ def test_workload_data_moves_full_size(td, name, bounded):
     td.moonep_dispatch(dims, pb, hid, recv)
     torch.cuda.synchronize()
     hflat, rflat = hid.view(wl.n_tok, wl.H), recv.view(-1, wl.H)
+    assert bool((src_d >= 0).all())
     for r in range(wl.R):
         sl = slice(r * wl.SK, (r + 1) * wl.SK)
         assert torch.equal(rflat[sl].view(torch.int16),
@@ -659,25 +685,35 @@ def test_workload_data_moves_full_size(td, name, bounded):
         assert np.array_equal(bf16_bits(rflat[int(lo):int(lo) + 64]), want)
     del hid_h, hflat, hid
 
-    # combine: y = seeded expert outputs; sampled tokens through the oracle
+    # combine: y = seeded expert outputs; every token through the oracle
     say("  combine")
     y = recv
     g = torch.Generator(device=DEV)
-    g.manual_seed(1234)
+    g.manual_seed(1234 + seed)
     for r in range(wl.R):
         y[r].copy_(torch.randn((wl.SK, wl.H), generator=g, device=DEV, dtype=torch.float32))
     w_d = torch.from_numpy(w).to(DEV)
     out = torch.empty((wl.R, wl.S, wl.H), dtype=torch.bfloat16, device=DEV)
     td.moonep_combine(dims, pb, y, w_d, out)
     torch.cuda.synchronize()
-    toks = np.unique(np.concatenate([rng.integers(0, wl.n_tok, 300), [0, wl.n_tok - 1]]))
-    dsel = p["dst"].reshape(-1, wl.K)[toks].reshape(-1)
-    y_rows = bf16_bits(y.view(-1, wl.H)[torch.from_numpy(dsel.astype(np.int64)).to(DEV)])
-    want = oracle.combine(np.arange(dsel.size, dtype=np.int32), wl.K, y_rows,
-                          w.reshape(-1, wl.K)[toks].reshape(-1), W.BF16, W.BF16)
-    got = bf16_bits(out.view(wl.n_tok, wl.H)[torch.from_numpy(toks).to(DEV)])
-    assert np.array_equal(got, want), "combine"
-    del y, recv, out
+    dst_tok = p["dst"].reshape(wl.n_tok, wl.K)
+    dst_d = torch.from_numpy(np.maximum(p["dst"], 0).astype(np.int64)).to(DEV)
+    wf = w.reshape(-1)
+    yflat, oflat = y.view(-1, wl.H), out.view(wl.n_tok, wl.H)
+    budget = 1 << 30
+    stage_y = HostStage(budget)
+    stage_o = HostStage(budget // wl.K + wl.row_bytes)
+    for t0, n in token_batches(wl.n_tok, wl.K, wl.row_bytes, budget):
+        a0, a1 = t0 * wl.K, (t0 + n) * wl.K
+        y_rows = stage_y.fetch(yflat.index_select(0, dst_d[a0:a1]))
+        want = oracle.combine(local_dst(dst_tok[t0:t0 + n]), wl.K, y_rows, wf[a0:a1], W.BF16,
+                              W.BF16)
+        got = stage_o.fetch(oflat[t0:t0 + n])
+        if not np.array_equal(got, want):
+            bad = np.nonzero((got != want).any(axis=1))[0]
+            raise AssertionError(f"combine differs at tokens {(t0 + bad[:8]).tolist()}")
+    say(f"  combine: all {wl.n_tok} tokens equal")
+    del y, recv, out, stage_y, stage_o
 
     # replicate: every materialised duplicate against the oracle's table
     say("  replicate")
@@ -691,29 +727,77 @@ def test_workload_data_moves_full_size(td, name, bounded):
             assert torch.equal(dup_w[r, b].view(torch.int16), ew[e].view(torch.int16))
     del ew, dup_w
 
-    # reduce: sampled experts with duplicates through the oracle
+    # reduce: every expert with duplicates through the oracle; the others untouched
     say("  reduce")
     dg, hg = W.make_grads(wl, seed, DEV)
     n = wl.block_elems
     nl = int(p["n_list"][0])
     exps = sorted(set(p["list_expert"][:nl].tolist()))
-    pick = [exps[0], exps[-1]] + [exps[i] for i in rng.integers(0, len(exps), 3)]
-    pick = sorted(set(pick))
-    untouched = [e for e in range(wl.E) if e not in set(exps)][:3]
-    before = {e: hg[e].cpu().numpy() for e in pick + untouched}
+    exps_d = torch.tensor(exps, dtype=torch.int64, device=DEV)
+    before = hg.index_select(0, exps_d)
+    hash0 = _row_hash(hg)
     td.moonep_reduce_dup_grads(dims, pb, dg, hg, n)
     torch.cuda.synchronize()
-    for e in pick:
+    most = max((sum(1 for q in range(int(p["dup_ptr"][e]), int(p["dup_ptr"][e + 1]))
+                    if p["list_b"][q] < wl.B) for e in exps), default=0)
+    stage = HostStage(4 * n * (most + 1))
+    for i, e in enumerate(exps):
         q0, q1 = int(p["dup_ptr"][e]), int(p["dup_ptr"][e + 1])
         sel = [q for q in range(q0, q1) if p["list_b"][q] < wl.B]
-        dup_rows = np.stack([dg[int(p["list_rank"][q]), int(p["list_b"][q])].cpu().numpy()
-                             for q in sel]) if sel else np.zeros((0, n), np.float32)
+        rows = [before[i]] + [dg[int(p["list_rank"][q]), int(p["list_b"][q])] for q in sel]
+        h = stage.fetch(torch.stack(rows)).copy()
         sub = {"dup_ptr": np.array([0, len(sel)], np.int32),
                "list_rank": np.zeros(len(sel), np.int32),
                "list_b": np.arange(len(sel), dtype=np.int32)}
-        want = oracle.reduce_dup_grads(sub, len(sel), dup_rows.reshape(1, len(sel), n),
-                                       before[e].reshape(1, n))
-        assert np.array_equal(f32_bits(hg[e]), want.reshape(-1).view(np.uint32)), f"reduce e={e}"
-    for e in untouched:
-        assert np.array_equal(f32_bits(hg[e]), before[e].view(np.uint32)), f"expert {e} touched"
-    say(f"  ok ({len(pick)} experts reduced checked, {len(untouched)} untouched sampled)")
+        want = oracle.reduce_dup_grads(sub, len(sel), h[1:].reshape(1, len(sel), n),
+                                       h[0].reshape(1, n))
+        got = stage.fetch(hg[e])
+        assert np.array_equal(got.view(np.uint32), want.reshape(-1).view(np.uint32)), \
+            f"reduce e={e}"
+    untouched = torch.ones(wl.E, dtype=torch.bool, device=DEV)
+    untouched[exps_d] = False
+    assert torch.equal(_row_hash(hg)[untouched], hash0[untouched]), "an expert without duplicates changed"
+    say(f"  ok (all {len(exps)} experts with duplicates reduced equal, "
+        f"{int(untouched.sum())} untouched)")
+
+
+@pytest.mark.parametrize("name", ["uniform", "zipf", "k3", "decode"])
+def test_workload_closed_forms_full_size(td, name):
+    """Properties that hold at any size, checked on every element at the full
+    workload shapes (K a power of two, bf16 rows), bitwise on the GPU:
+    - identity experts (y = recv) with weights 1/K: combine gives hidden back;
+    - the backward of dispatch applied to a dispatch gives K * hidden (exact);
+    - unit weights: grad_y of every slot is the grad_out row of its token."""
+    wl = W.WORKLOADS[name]
+    assert wl.K & (wl.K - 1) == 0 and wl.dtype == W.BF16
+    dims = _dims(td, wl)
+    say(f"closed forms {name}: {dims}")
+    ids, _ = W.make_routing(wl, 5)
+    pb, _ = run_plan(td, dims, ids, DEV)
+    p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids)
+    assert np.array_equal(read_plan(td, dims, pb)["dst"], p["dst"])
+    hid = W.make_hidden(wl, 5, DEV)
+    recv = torch.empty((wl.R, wl.SK, wl.H), dtype=hid.dtype, device=DEV)
+    td.moonep_dispatch(dims, pb, hid, recv)
+    w_d = torch.full((wl.R, wl.S, wl.K), 1.0 / wl.K, dtype=torch.float32, device=DEV)
+    out = torch.empty_like(hid)
+    td.moonep_combine(dims, pb, recv, w_d, out)
+    back = torch.empty_like(hid)
+    td.moonep_dispatch_backward(dims, pb, recv, back)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), hid.view(torch.int16)), "combine of identity experts"
+    assert torch.equal(back.view(torch.int16),
+                       (hid.float() * wl.K).to(torch.bfloat16).view(torch.int16)), \
+        "backward of dispatch of a dispatch"
+    del out, back
+    gout = W.dense((wl.R, wl.S, wl.H), W.BF16, 1.0, 6, "hidden", DEV)
+    w_d.fill_(1.0)
+    td.moonep_combine_backward(dims, pb, gout, w_d, None, recv, None)
+    torch.cuda.synchronize()
+    src_d = torch.from_numpy(p["src"].astype(np.int64)).to(DEV)
+    gflat, rflat = gout.view(wl.n_tok, wl.H), recv.view(-1, wl.H)
+    for r in range(wl.R):
+        sl = slice(r * wl.SK, (r + 1) * wl.SK)
+        assert torch.equal(rflat[sl].view(torch.int16),
+                           gflat[src_d[sl] // wl.K].view(torch.int16)), f"grad_y rank {r}"
+    say("  ok")

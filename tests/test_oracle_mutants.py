@@ -18,6 +18,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
+import oracle
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moonep_oracle.c")
 PINS = "tests/test_oracle_pins.py"
@@ -157,13 +159,14 @@ def _build(src_text, out_dir, name):
     so = os.path.join(out_dir, name + ".so")
     with open(c, "w") as f:
         f.write(src_text)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-                           "-shared", "-fPIC", "-o", so, c, "-lm"])
+    subprocess.check_call(["gcc"] + oracle.CFLAGS + ["-o", so, c, "-lm"])
     return so
 
 
 def _run_pins(lib, files):
-    env = dict(os.environ, MOONEP_ORACLE_LIB=lib, PYTHONDONTWRITEBYTECODE="1")
+    # one thread per child: the children already run side by side
+    env = dict(os.environ, MOONEP_ORACLE_LIB=lib, PYTHONDONTWRITEBYTECODE="1",
+               OMP_NUM_THREADS="1")
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
            "-m", "not gpu", "-k", "not 4-4-1-2"] + files
     p = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
