@@ -564,7 +564,17 @@ def main():
         print(f"# graph replay: {graph}", file=sys.stderr, flush=True)
     plan_lat = None
     if args.plan_iters > 0 and not args.copy_calibration:
+        # the form moonep_plan takes for these dims, then the other one forced
+        launches = td.moonep_plan_layout(dims).plan_launches
         plan_lat = plan_latency(plan_fn, dims, ids_d, plan_buf, stream, args.plan_iters)
+        plan_lat["launches"] = launches
+        other = td.PLAN_FOUR_LAUNCH if launches == 2 else td.PLAN_TWO_LAUNCH
+        bflag = td.PLAN_BOUNDED if args.plan == "bounded" else 0
+        plan_lat["other_form"] = plan_latency(
+            lambda d, i, b: td.moonep_plan_ex(d, i, b, other | bflag), dims, ids_d, plan_buf,
+            stream, args.plan_iters)
+        plan_lat["other_form"]["launches"] = 4 if launches == 2 else 2
+        plan_fn(dims, ids_d, plan_buf)  # leave the default form's plan in the buffer
         print(f"# plan latency: {plan_lat}", file=sys.stderr, flush=True)
     ceil = None
     if not args.no_ceiling and not args.copy_calibration:

@@ -122,8 +122,11 @@ typedef struct moonep_layout {
     int32_t dcap;          /* max(1, min(SK, E - G)): most duplicates one rank can hold */
     int32_t pcap;          /* E + R: room for the global duplicate list                 */
     int32_t n_tiles;       /* token tiles of the plan kernels                           */
-    int32_t tile_tokens;   /* tokens per tile: 4096, 2048 or 1024 entries rounded down
-                              to whole tokens, the largest giving at least 256 tiles  */
+    int32_t tile_tokens;   /* tokens per tile: 1024, 2048 or 4096 entries rounded down
+                              to whole tokens (see plan_launches)                     */
+    int32_t plan_launches; /* kernel launches of moonep_plan: 2 when a tile size keeps
+                              n_tiles * E <= 65536 (the smallest such tile is used),
+                              else 4 (the largest tile giving at least 256 tiles)     */
     int64_t status, maxT, maxvio, T, hoff, L, keep, O, D, Opre, Dpre, dst, src;
     int64_t n_dup, dup_expert, dup_start, dup_count, seg_ptr, seg_expert;
     int64_t n_list, list_expert, list_rank, list_b, dup_ptr;
@@ -152,10 +155,32 @@ int moonep_plan_layout(const moonep_dims *dims, moonep_layout *out);
  * The result depends on the ids only (B only sets MOONEP_STATUS_OVER_B) and is
  * bit-for-bit deterministic.
  *
- * Four kernel launches. The plan buffer needs no initialisation; one plan buffer
- * must not be used by two calls that run at the same time.
+ * moonep_plan_layout().plan_launches kernel launches: four (per-tile counts, a
+ * scan of the counts over tiles, a one-workgroup solve, per-tile assignment), or
+ * two for problems with few tiles (the decode shape): the per-tile counts, then
+ * one launch in which every workgroup sums all tile counts, runs the same
+ * deterministic solve and assigns its own tile -- the scheduling is "online with
+ * near-zero overhead" (news.hamidun.com EN, "How MoonEP works"), and the launch
+ * count is what a small step pays for. Both forms give the same plan bit for bit.
+ * The plan buffer needs no initialisation; one plan buffer must not be used by
+ * two calls that run at the same time.
  */
 int moonep_plan(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf, void *stream);
+
+/*
+ * moonep_plan_ex -- moonep_plan with options, OR'd into flags:
+ *   MOONEP_PLAN_BOUNDED      the plan of moonep_plan_bounded instead of the water-fill
+ *   MOONEP_PLAN_FOUR_LAUNCH  the four-launch form whatever plan_launches says
+ *   MOONEP_PLAN_TWO_LAUNCH   the two-launch form whatever plan_launches says (at
+ *                            large shapes every workgroup then reads n_tiles * E
+ *                            counts and runs the whole solve: correct but slow)
+ * The results do not depend on the form. Unknown bits, or both forms at once,
+ * return MOONEP_ERR_DIMS. moonep_plan is moonep_plan_ex with flags = 0 and
+ * moonep_plan_bounded with flags = MOONEP_PLAN_BOUNDED.
+ */
+enum { MOONEP_PLAN_BOUNDED = 1, MOONEP_PLAN_FOUR_LAUNCH = 2, MOONEP_PLAN_TWO_LAUNCH = 4 };
+int moonep_plan_ex(const moonep_dims *dims, const int32_t *topk_ids, void *plan_buf, int32_t flags,
+                   void *stream);
 
 /*
  * moonep_plan_bounded -- the same plan with at most B duplicates per rank where

@@ -18,14 +18,25 @@ def dims_for(td, R, E, K, S, B, H, dtype):
     return td.Dims(R, E, K, S, B, dtype, H)
 
 
-def run_plan(td, dims, ids_np, dev, plan_buf=None, bounded=False):
+def run_plan(td, dims, ids_np, dev, plan_buf=None, bounded=False, form=None):
+    """Plan through the C ABI: moonep_plan / moonep_plan_bounded, or with form
+    "two" / "four" the launch form forced through moonep_plan_ex."""
     import torch
     if plan_buf is None:
         plan_buf = td.new_plan_buffer(dims, dev)
     ids_d = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
-    (td.moonep_plan_bounded if bounded else td.moonep_plan)(dims, ids_d, plan_buf)
+    if form is None:
+        (td.moonep_plan_bounded if bounded else td.moonep_plan)(dims, ids_d, plan_buf)
+    else:
+        flags = {"two": td.PLAN_TWO_LAUNCH, "four": td.PLAN_FOUR_LAUNCH}[form]
+        td.moonep_plan_ex(dims, ids_d, plan_buf, flags | (td.PLAN_BOUNDED if bounded else 0))
     torch.cuda.synchronize()
     return plan_buf, ids_d
+
+
+def other_form(td, dims):
+    """The launch form moonep_plan does not take for these dims."""
+    return "four" if td.moonep_plan_layout(dims).plan_launches == 2 else "two"
 
 
 def read_plan(td, dims, plan_buf):

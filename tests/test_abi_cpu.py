@@ -61,7 +61,8 @@ def _dims(td, R=32, E=896, K=16, S=4096, B=28, dtype=1, H=7168):
 
 @pytest.mark.parametrize("shape", [(32, 896, 16, 4096, 28, 1, 7168), (4, 16, 2, 64, 4, 0, 128),
                                    (64, 896, 16, 128, 4, 1, 7168), (1, 8, 8, 3, 0, 0, 4),
-                                   (1024, 1024, 64, 1, 1, 1, 8)])
+                                   (1024, 1024, 64, 1, 1, 1, 8), (16, 256, 8, 8192, 16, 1, 4096),
+                                   (8, 64, 8, 4096, 8, 1, 2048)])
 def test_layout(td, shape):
     d = td.Dims(*shape)
     lay = td.moonep_plan_layout(d)
@@ -69,11 +70,17 @@ def test_layout(td, shape):
     G, SK = E // R, S * K
     assert lay.dcap == max(1, min(SK, E - G))
     assert lay.pcap == E + R
-    # the largest tile of 4096, 2048 or 1024 entries that still gives 256 tiles
-    n_ent = R * S * K
-    tile = next((t for t in (4096, 2048, 1024) if n_ent // t >= 256), 1024)
+    # two launches with the smallest tile of 1024, 2048 or 4096 entries that keeps
+    # n_tiles * E <= 65536; else four with the largest tile giving 256 tiles
+    n_ent, n_tok = R * S * K, R * S
+    fused = [t for t in (1024, 2048, 4096) if -(-n_tok // (t // K)) * E <= 65536]
+    if fused:
+        tile, launches = fused[0], 2
+    else:
+        tile, launches = next((t for t in (4096, 2048, 1024) if n_ent // t >= 256), 1024), 4
+    assert lay.plan_launches == launches
     assert lay.tile_tokens == tile // K
-    assert lay.n_tiles == -(-(R * S) // lay.tile_tokens)
+    assert lay.n_tiles == -(-n_tok // lay.tile_tokens)
     sizes = {"status": 4, "maxT": 4, "maxvio": 8, "T": 4 * E, "hoff": 4 * E, "L": 4 * R,
              "keep": 4 * R, "O": 4 * R, "D": 4 * R, "Opre": 4 * (R + 1), "Dpre": 4 * (R + 1),
              "dst": 4 * R * SK, "src": 4 * R * SK, "n_dup": 4 * R,
@@ -149,6 +156,28 @@ def test_pointer_and_size_errors(td):
                                    ctypes.byref(n)) == -1
     for rc in (0, -1, -2, -3, -4, 5):
         assert td.moonep_strerror(rc)
+
+
+def test_workload_launch_forms(td):
+    """Which workloads take the two-launch plan, and with which tiles."""
+    want = {"tiny": (2, 1024), "uniform": (2, 1024), "zipf": (2, 4096), "k3": (4, 4096),
+            "decode": (2, 2048)}
+    import workloads as W
+    for name, (launches, tile) in want.items():
+        wl = W.WORKLOADS[name]
+        lay = td.moonep_plan_layout(td.Dims(wl.R, wl.E, wl.K, wl.S, wl.B, wl.dtype, wl.H))
+        assert (lay.plan_launches, lay.tile_tokens * wl.K) == (launches, tile), name
+
+
+def test_plan_ex_flag_errors(td):
+    lib = td._lib
+    ok = ctypes.c_void_p(1 << 20)
+    d = _dims(td)
+    for flags in (8, 16, -1, td.PLAN_TWO_LAUNCH | td.PLAN_FOUR_LAUNCH,
+                  td.PLAN_BOUNDED | td.PLAN_TWO_LAUNCH | td.PLAN_FOUR_LAUNCH):
+        assert lib.moonep_plan_ex(ctypes.byref(d), ok, ok, flags, None) == -1, flags
+    assert lib.moonep_plan_ex(ctypes.byref(d), None, ok, td.PLAN_BOUNDED, None) == -2
+    assert lib.moonep_plan_ex(ctypes.byref(_dims(td, E=900)), ok, ok, 0, None) == -1
 
 
 def test_noscratch_argument_errors(td):

@@ -23,7 +23,7 @@ import torch
 import oracle
 import workloads as W
 from tests.gpu_common import (PLAN_INT_KEYS, HostStage, assert_plan_equal, bf16_bits, f32_bits,
-                              local_dst, read_plan, run_plan, say, token_batches)
+                              local_dst, other_form, read_plan, run_plan, say, token_batches)
 from tests.invariants import check_plan
 
 pytestmark = pytest.mark.gpu
@@ -70,8 +70,13 @@ SMALL = [
     _wl("k6", 4, 48, 6, 777, 4, 64, W.BF16, 2.0),
     _wl("k12_f32", 8, 96, 12, 300, 6, 40, W.F32, 1.5),
     _wl("k40", 2, 80, 40, 120, 8, 64, W.BF16, 1.0),
-    # 2048-entry plan tiles (two 64-entry chunks per assign wave), ragged last tile
-    _wl("tiles_2048", 8, 64, 8, 8200, 8, 64, W.BF16, 2.0),
+    # four launches with 2048-entry plan tiles (two 64-entry chunks per assign
+    # wave), ragged last tile
+    _wl("tiles_2048", 8, 1024, 8, 8200, 8, 64, W.BF16, 2.0),
+    # two launches with 2048- and 4096-entry tiles (n_tiles * E just within the
+    # fused kernel's count budget)
+    _wl("fused_2048", 8, 1024, 8, 1500, 8, 64, W.BF16, 2.0),
+    _wl("fused_4096", 8, 1024, 8, 3000, 8, 64, W.BF16, 2.0),
     # the tiny workload as given: fp32 rows, fp32 [128, 256] weight blocks
     W.WORKLOADS["tiny"],
     # 7 and 16 chunks per lane (rows of 425 or 426 and 1000 16-byte chunks,
@@ -108,6 +113,11 @@ def _full_case(td, wl, ids, w, seed, bounded=False):
     assert_plan_equal(g, p)
     valid = bool(np.all((ids >= 0) & (ids < wl.E)))
     check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g, valid_input=valid)
+    # the other launch form gives the same plan
+    form = other_form(td, dims)
+    buf2, _ = run_plan(td, dims, ids, DEV, bounded=bounded, form=form)
+    assert_plan_equal(read_plan(td, dims, buf2), p)
+    del buf2
 
     hidden = W.make_hidden(wl, seed)
     hid_d = hidden.to(DEV)
@@ -178,14 +188,15 @@ def test_hand_worked_examples_on_gpu(td):
         dims = td.Dims(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], W.F32, 4)
         say(f"golden {os.path.basename(path)}")
         ids = np.array(ex["ids"], np.int32)
-        plan_buf, _ = run_plan(td, dims, ids, DEV)
-        g = read_plan(td, dims, plan_buf)
-        SK = ex["S"] * ex["K"]
-        x = ex["expect"]
-        assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
-        assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
-        assert float(g["maxvio"][0]) == x["maxvio"]
-        assert_plan_equal(g, oracle.plan(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], ids))
+        for form in ("two", "four"):
+            plan_buf, _ = run_plan(td, dims, ids, DEV, form=form)
+            g = read_plan(td, dims, plan_buf)
+            SK = ex["S"] * ex["K"]
+            x = ex["expect"]
+            assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
+            assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
+            assert float(g["maxvio"][0]) == x["maxvio"]
+            assert_plan_equal(g, oracle.plan(ex["R"], ex["E"], ex["K"], ex["S"], ex["B"], ids))
 
 
 def test_bounded_hand_worked_examples_on_gpu(td):
@@ -201,23 +212,29 @@ def test_bounded_hand_worked_examples_on_gpu(td):
         dims = td.Dims(R, E, K, S, B, W.F32, 4)
         say(f"golden {os.path.basename(path)}")
         ids = np.array(ex["ids"], np.int32)
-        plan_buf, _ = run_plan(td, dims, ids, DEV, bounded=True)
-        g = read_plan(td, dims, plan_buf)
-        SK, G = S * K, E // R
-        x = ex["expect"]
-        assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
-        assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
-        assert float(g["maxvio"][0]) == x["maxvio"]
-        got_dups = [[r, b, int(g["dup_expert"][r, b]), int(g["dup_start"][r, b]),
-                     int(g["dup_count"][r, b])] for r in range(R) for b in range(int(g["n_dup"][r]))]
-        assert got_dups == x["dups"]
-        nl = int(g["n_list"][0])
-        assert [[int(g["list_expert"][i]), int(g["list_rank"][i]), int(g["list_b"][i])]
-                for i in range(nl)] == x["list"]
-        for r in range(R):
-            ns = G + int(g["n_dup"][r])
-            assert g["seg_ptr"][r, :ns + 1].tolist() == x["seg_ptr"][r]
-        assert_plan_equal(g, oracle.plan(R, E, K, S, B, ids, bounded=True))
+        for form in ("two", "four"):
+            plan_buf, _ = run_plan(td, dims, ids, DEV, bounded=True, form=form)
+            _check_bounded_golden(td, dims, ex, ids, plan_buf)
+
+
+def _check_bounded_golden(td, dims, ex, ids, plan_buf):
+    R, E, K, S, B = ex["R"], ex["E"], ex["K"], ex["S"], ex["B"]
+    g = read_plan(td, dims, plan_buf)
+    SK, G = S * K, E // R
+    x = ex["expect"]
+    assert [[d // SK, d % SK] for d in g["dst"].tolist()] == x["dst_rank_slot"]
+    assert g["n_dup"].tolist() == x["n_dup"] and int(g["status"][0]) == x["status"]
+    assert float(g["maxvio"][0]) == x["maxvio"]
+    got_dups = [[r, b, int(g["dup_expert"][r, b]), int(g["dup_start"][r, b]),
+                 int(g["dup_count"][r, b])] for r in range(R) for b in range(int(g["n_dup"][r]))]
+    assert got_dups == x["dups"]
+    nl = int(g["n_list"][0])
+    assert [[int(g["list_expert"][i]), int(g["list_rank"][i]), int(g["list_b"][i])]
+            for i in range(nl)] == x["list"]
+    for r in range(R):
+        ns = G + int(g["n_dup"][r])
+        assert g["seg_ptr"][r, :ns + 1].tolist() == x["seg_ptr"][r]
+    assert_plan_equal(g, oracle.plan(R, E, K, S, B, ids, bounded=True))
 
 
 @PLANS
@@ -621,9 +638,12 @@ def test_workload_plans_all_seeds(td, name, bounded):
     for seed in (0, 1, 2):
         say(f"plan {name} seed {seed} bounded={bounded}")
         ids, _ = W.make_routing(wl, seed)
+        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
+        for form in ("two", "four"):
+            run_plan(td, dims, ids, DEV, pb, bounded=bounded, form=form)
+            assert_plan_equal(read_plan(td, dims, pb), p)
         run_plan(td, dims, ids, DEV, pb, bounded=bounded)
         g = read_plan(td, dims, pb)
-        p = oracle.plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, bounded=bounded)
         assert_plan_equal(g, p)
         if seed == 0:
             check_plan(wl.R, wl.E, wl.K, wl.S, wl.B, ids, g)

@@ -30,8 +30,9 @@ BF16 = 1
 STATIC_SCRATCH_BYTES = 8 << 20  # MOONEP_STATIC_SCRATCH_BYTES
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 OP_DISPATCH, OP_COMBINE = 1, 2
+PLAN_BOUNDED, PLAN_FOUR_LAUNCH, PLAN_TWO_LAUNCH = 1, 2, 4
 
-ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_bounded",
+ENTRY_POINTS = ("moonep_plan_layout", "moonep_plan", "moonep_plan_ex", "moonep_plan_bounded",
                 "moonep_plan_noscratch", "moonep_dispatch", "moonep_replicate",
                 "moonep_combine", "moonep_reduce_dup_grads", "moonep_combine_backward",
                 "moonep_dispatch_backward", "moonep_launch_count", "moonep_strerror")
@@ -60,7 +61,8 @@ _LAYOUT_OFFSETS = ("status", "maxT", "maxvio", "T", "hoff", "L", "keep", "O", "D
 class Layout(ctypes.Structure):
     _fields_ = ([("bytes", ctypes.c_int64), ("persist_bytes", ctypes.c_int64),
                  ("dcap", ctypes.c_int32), ("pcap", ctypes.c_int32),
-                 ("n_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32)]
+                 ("n_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
+                 ("plan_launches", ctypes.c_int32)]
                 + [(n, ctypes.c_int64) for n in _LAYOUT_OFFSETS])
 
 
@@ -69,6 +71,7 @@ _P_DIMS, _P_LAY = ctypes.POINTER(Dims), ctypes.POINTER(Layout)
 _lib.moonep_plan_layout.argtypes = [_P_DIMS, _P_LAY]
 _lib.moonep_plan.argtypes = [_P_DIMS, _vp, _vp, _vp]
 _lib.moonep_plan_bounded.argtypes = [_P_DIMS, _vp, _vp, _vp]
+_lib.moonep_plan_ex.argtypes = [_P_DIMS, _vp, _vp, _i32, _vp]
 _lib.moonep_plan_noscratch.argtypes = [_P_DIMS, _vp, _vp, _i32, _vp]
 _lib.moonep_dispatch.argtypes = [_P_DIMS, _vp, _vp, _vp, _vp]
 _lib.moonep_replicate.argtypes = [_P_DIMS, _vp, _vp, _vp, _i64, _vp]
@@ -159,6 +162,16 @@ def moonep_plan_bounded(dims: Dims, topk_ids, plan_buf, stream=None) -> None:
     pb = _ptr(plan_buf, "plan_buf", None, lay.bytes)
     _check(_lib.moonep_plan_bounded(ctypes.byref(dims), ids, pb, _stream(stream, plan_buf)),
            "moonep_plan_bounded")
+
+
+def moonep_plan_ex(dims: Dims, topk_ids, plan_buf, flags: int = 0, stream=None) -> None:
+    """moonep_plan with options: PLAN_BOUNDED, PLAN_FOUR_LAUNCH, PLAN_TWO_LAUNCH."""
+    torch = _torch()
+    lay = moonep_plan_layout(dims)
+    ids = _ptr(topk_ids, "topk_ids", torch.int32, 4 * dims.R * dims.S * dims.K)
+    pb = _ptr(plan_buf, "plan_buf", None, lay.bytes)
+    _check(_lib.moonep_plan_ex(ctypes.byref(dims), ids, pb, int(flags), _stream(stream, plan_buf)),
+           "moonep_plan_ex")
 
 
 def moonep_plan_noscratch(dims: Dims, topk_ids, plan_buf, bounded: bool = False,

@@ -60,6 +60,7 @@ PlanShape shape_of(const moonep_dims *d, const moonep_layout &lay) {
     while ((1 << bits) < d->E) ++bits;
     s.id_bits = bits;
     s.inv_k = 1.0f / (float)d->K;
+    s.launches = lay.plan_launches;
     return s;
 }
 
@@ -159,12 +160,28 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     if (dcap < 1) dcap = 1;
     l.dcap = (int32_t)dcap;
     l.pcap = (int32_t)(E + R);
-    // the largest tile (4096, 2048 or 1024 entries) that still gives kTileTarget
-    // tiles, so that small problems spread over more of the device
-    int64_t tile_entries = kTileEntries;
-    while (tile_entries > kMinTileEntries && NE / tile_entries < kTileTarget) tile_entries /= 2;
+    // Two launches when a tile of 1024, 2048 or 4096 entries keeps the counts that
+    // every workgroup of the fused kernel reads (n_tiles * E) within
+    // kFusedMaxCounts: the smallest such tile. Else four launches with the largest
+    // tile that still gives kTileTarget tiles, so that small problems spread over
+    // more of the device.
+    auto tiles_of = [&](int64_t entries) {
+        const int64_t tt = entries / d->K;
+        return (n_tok + tt - 1) / tt;
+    };
+    int64_t tile_entries = 0;
+    for (int64_t te = kMinTileEntries; te <= kTileEntries; te *= 2)
+        if (tiles_of(te) * E <= kFusedMaxCounts) {
+            tile_entries = te;
+            break;
+        }
+    l.plan_launches = tile_entries > 0 ? 2 : 4;
+    if (tile_entries == 0) {
+        tile_entries = kTileEntries;
+        while (tile_entries > kMinTileEntries && NE / tile_entries < kTileTarget) tile_entries /= 2;
+    }
     l.tile_tokens = (int32_t)(tile_entries / d->K);
-    l.n_tiles = (int32_t)((n_tok + l.tile_tokens - 1) / l.tile_tokens);
+    l.n_tiles = (int32_t)tiles_of(tile_entries);
     int64_t off = 0;
     auto take = [&off](int64_t bytes) {
         const int64_t o = off;
@@ -214,25 +231,32 @@ int moonep_plan_layout(const moonep_dims *d, moonep_layout *out) {
     return MOONEP_OK;
 }
 
-static int plan_common(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, void *stream,
-                       bool bounded) {
+int moonep_plan_ex(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, int32_t flags,
+                   void *stream) {
     moonep_layout l;
     int rc = moonep_plan_layout(d, &l);
     if (rc != MOONEP_OK) return rc;
+    const int32_t known = MOONEP_PLAN_BOUNDED | MOONEP_PLAN_FOUR_LAUNCH | MOONEP_PLAN_TWO_LAUNCH;
+    if ((flags & ~known) != 0 ||
+        ((flags & MOONEP_PLAN_FOUR_LAUNCH) && (flags & MOONEP_PLAN_TWO_LAUNCH)))
+        return MOONEP_ERR_DIMS;
     if (!aligned16(topk_ids) || !aligned16(plan_buf)) return MOONEP_ERR_PTR;
-    const PlanShape sh = shape_of(d, l);
+    PlanShape sh = shape_of(d, l);
+    if (flags & MOONEP_PLAN_FOUR_LAUNCH) sh.launches = 4;
+    if (flags & MOONEP_PLAN_TWO_LAUNCH) sh.launches = 2;
     (void)hipGetLastError();
-    return launch_rc(launch_plan(sh, topk_ids, resolve(l, plan_buf), bounded,
+    return launch_rc(launch_plan(sh, topk_ids, resolve(l, plan_buf),
+                                 (flags & MOONEP_PLAN_BOUNDED) != 0,
                                  static_cast<hipStream_t>(stream)));
 }
 
 int moonep_plan(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf, void *stream) {
-    return plan_common(d, topk_ids, plan_buf, stream, false);
+    return moonep_plan_ex(d, topk_ids, plan_buf, 0, stream);
 }
 
 int moonep_plan_bounded(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf,
                         void *stream) {
-    return plan_common(d, topk_ids, plan_buf, stream, true);
+    return moonep_plan_ex(d, topk_ids, plan_buf, MOONEP_PLAN_BOUNDED, stream);
 }
 
 int moonep_plan_noscratch(const moonep_dims *d, const int32_t *topk_ids, void *plan_buf,

@@ -16,6 +16,9 @@ constexpr int kMaxK = 64;          // one entry of a token per lane
 constexpr int kTileEntries = 4096; // most entries per plan tile (rounded down to whole tokens)
 constexpr int kMinTileEntries = 1024;  // fewest: one 64-entry chunk per wave of a 16-wave tile
 constexpr int kTileTarget = 256;   // tiles wanted to spread the plan over the device
+// The two-launch plan (k_count, then k_plan_fused) is taken when some tile size
+// keeps the counts every workgroup reads (n_tiles * E) at or below this.
+constexpr int kFusedMaxCounts = 1 << 16;
 constexpr int kPlanThreads = 256;  // count / assign workgroup
 constexpr int kSolveThreads = 1024;
 
@@ -43,6 +46,7 @@ struct PlanShape {
     int32_t tile_chunks;  // 64-entry chunks per wave of an assign tile (1 .. 4)
     int32_t id_bits;      // bits needed to tell expert ids apart (ceil log2 E, >= 1)
     float inv_k;          // 1/K rounded to nearest: token of an in-tile entry index
+    int32_t launches;     // 2: k_count + k_plan_fused; 4: k_count, k_scan, solve, k_assign
 };
 
 // Typed pointers into a plan buffer; the second form takes the plan kernels'

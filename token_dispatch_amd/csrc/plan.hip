@@ -49,6 +49,7 @@ static_assert(kMaxE <= kAssignThreads && kMaxR <= kAssignThreads && kMaxE <= kSo
 static_assert((1 << kMaxIdBits) >= kMaxE, "ids fit the ballot bit slices");
 static_assert(kSolveThreads == kAssignThreads, "assign uses the solve's block scan");
 static_assert(kTileEntries <= (1 << 22), "an in-tile index and an id share a word");
+static_assert(kTileEntries < (1 << 16), "a tile's count of one expert fits 16 bits");
 static_assert(kMaxE <= 1024 && (kMaxE & (kMaxE - 1)) == 0, "expert ids fit the 10-bit field of a packed placement key");
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
@@ -140,7 +141,10 @@ constexpr int tpt_of(int kmax) {
     return (kTileEntries / (kmax == 1 ? 1 : kmax / 2 + 1) + kPlanThreads - 1) / kPlanThreads;
 }
 
-template <int KMAX>
+// U16: the counts are stored as 16-bit words (a tile holds at most kTileEntries
+// <= 65535 entries), for the two-launch plan whose every workgroup reads them all;
+// the four-launch plan keeps 32-bit words, which k_scan turns into prefixes.
+template <int KMAX, bool U16>
 __global__ __launch_bounds__(kPlanThreads) void k_count(const int32_t *__restrict__ ids,
                                                         PlanShape sh,
                                                         int32_t *__restrict__ tile_counts,
@@ -220,8 +224,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(const int32_t *__restric
     }
     if (st) atomicOr(&s_st, st);
     __syncthreads();
-    int32_t *out = tile_counts + (int64_t)tile * sh.E;
-    for (int e = tid; e < sh.E; e += kPlanThreads) out[e] = s_hist[e];
+    if constexpr (U16) {
+        uint16_t *out = reinterpret_cast<uint16_t *>(tile_counts) + (int64_t)tile * sh.E;
+        for (int e = tid; e < sh.E; e += kPlanThreads) out[e] = (uint16_t)s_hist[e];
+    } else {
+        int32_t *out = tile_counts + (int64_t)tile * sh.E;
+        for (int e = tid; e < sh.E; e += kPlanThreads) out[e] = s_hist[e];
+    }
     if (tid == 0) tile_status[tile] = s_st;
 }
 
@@ -287,19 +296,20 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(PlanShape sh,
 // The part both solves share: tile status bits and maxT (into *s_status,
 // *s_maxT), T in LDS, the exclusive prefix of T (s_cum), home offsets and home
 // load, keep / overflow / deficit per rank (written to the plan and to s_keep,
-// s_O, s_D). Every thread of the 1024-thread workgroup must call it.
+// s_O, s_D). Every thread of the 1024-thread workgroup must call it, with Te =
+// T of expert threadIdx.x (0 beyond E) and st = its share of the OR of the
+// tiles' status words.
 struct Head {
     int Te, hoff, keep, O, D;
 };
 
-__device__ Head solve_head(const PlanShape &sh, const PlanPtrs &p, int *s_T, int *s_cum, int *s_keep,
-                           int *s_O, int *s_D, int *s_w, int *s_status, int *s_maxT) {
+__device__ Head solve_head(const PlanShape &sh, const PlanPtrs &p, int Te, int st, int *s_T,
+                           int *s_cum, int *s_keep, int *s_O, int *s_D, int *s_w, int *s_status,
+                           int *s_maxT) {
     const int tid = threadIdx.x, lane = lane_id();
     const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
     Head h{};
-    h.Te = tid < E ? p.T[tid] : 0;
-    int st = 0;
-    for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
+    h.Te = Te;
     if (tid == 0) {
         *s_status = 0;
         *s_maxT = 0;
@@ -439,7 +449,8 @@ inline size_t solve_lds_bytes(const PlanShape &sh, bool bounded) {
 
 // ---------------------------------------------------------------- water-fill solve
 // One 1024-thread workgroup; smem holds wf_lds() ints.
-__device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t *smem) {
+__device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t *smem, int Te,
+                                int st) {
     WfLds L;
     wf_lds(sh.E, sh.R, sh.pcap, smem, &L);
     int *const s_T = L.T, *const s_cum = L.cum, *const s_ovpre = L.ovpre, *const s_ovp = L.ovp;
@@ -450,7 +461,7 @@ __device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t 
 
     const int tid = threadIdx.x;
     const int E = sh.E, R = sh.R, G = sh.G, SK = sh.SK;
-    const Head h = solve_head(sh, p, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
+    const Head h = solve_head(sh, p, Te, st, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
     // each expert's overflow: the part of its home list [hoff, hoff + T) at or
     // beyond S*K; in the global overflow order (home rank, expert, token, k) --
     // with contiguous homes simply expert order -- it is [ovpre, ovpre + ov).
@@ -571,9 +582,19 @@ __device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t 
     solve_tail(sh, p, totNZ, &s_status, &s_maxT);
 }
 
+// T (from k_scan) and this thread's share of the tiles' status words.
+__device__ __forceinline__ void solve_inputs(const PlanShape &sh, const PlanPtrs &p, int &Te, int &st) {
+    const int tid = threadIdx.x;
+    Te = tid < sh.E ? p.T[tid] : 0;
+    st = 0;
+    for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
+}
+
 __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
-    solve_waterfill(sh, p, smem);
+    int Te, st;
+    solve_inputs(sh, p, Te, st);
+    solve_waterfill(sh, p, smem, Te, st);
 }
 
 // ---------------------------------------------------------------- k_solve_bounded
@@ -716,7 +737,8 @@ __device__ __forceinline__ int place_pieces(const PlaceArgs &a, bool packed) {
 }
 
 // One 1024-thread workgroup; smem holds bd_lds() ints.
-__device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *smem) {
+__device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *smem, int Te,
+                              int st) {
     BdLds L;
     bd_lds(sh.E, sh.R, sh.pcap, smem, &L);
     uint64_t *const s_bkey = L.bkey;
@@ -730,7 +752,7 @@ __device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *s
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
     const int E = sh.E, R = sh.R, G = sh.G, B = sh.B;
-    const Head h = solve_head(sh, p, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
+    const Head h = solve_head(sh, p, Te, st, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
 
     // 1. overflow of each overloaded rank, from its largest experts
     int ov = 0;
@@ -866,7 +888,9 @@ __device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *s
 
 __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
-    solve_bounded(sh, p, smem);
+    int Te, st;
+    solve_inputs(sh, p, Te, st);
+    solve_bounded(sh, p, smem, Te, st);
 }
 
 // ---------------------------------------------------------------- assign
@@ -965,11 +989,12 @@ struct TableRegs {
 // Every thread issues every load (indices clamped into range), so that the
 // number of loads in flight is the same on every path and the ranks can start
 // as soon as the ids are in, with the table loads still outstanding.
-__device__ __forceinline__ TableRegs fetch_tables(const PlanShape &sh, const PlanPtrs &p, int tile) {
+__device__ __forceinline__ TableRegs fetch_tables(const PlanShape &sh, const PlanPtrs &p, int tile,
+                                                  bool scanned_base) {
     const int tid = threadIdx.x, E = sh.E, R = sh.R;
     const int e = min(tid, E - 1), r = min(tid, R);
     TableRegs g;
-    g.tbase = p.tile_counts[(int64_t)tile * E + e];
+    g.tbase = scanned_base ? p.tile_counts[(int64_t)tile * E + e] : 0;
     g.kept = p.kept[e];
     g.koff = p.koff[e];
     g.dup_ptr = p.dup_ptr[e];
@@ -1191,23 +1216,14 @@ __device__ __forceinline__ void plan_tails(const PlanShape &sh, const PlanPtrs &
     }
 }
 
-// ---------------------------------------------------------------- k_assign
-// Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
-// compiler budget scalar registers for that (the plan pointers would otherwise
-// hold enough of them to allow only one).
-__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
-    extern __shared__ int32_t smem[];
+// The assign passes over one tile, once its ids are in idv and the plan tables
+// the placement needs are in regs (fetch_tables). smem holds assign_lds_bytes().
+__device__ __forceinline__ void assign_tile(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
+                                            const int (&idv)[kChunks], const TableRegs &regs,
+                                            int32_t *smem) {
     uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
     AsgTables tb;
     asg_tables(sh.E, sh.R, sh.pcap, tile_cap(sh), smem + pos_ints(sh), &tb);
-    const Tile t = tile_of(sh, blockIdx.x);
-
-    // loads first, all in flight: this wave's ids, then the tables, which are
-    // only needed once the ranks are taken
-    int idv[kChunks];
-    load_ids(sh, ids, t, idv);
-    const TableRegs regs = fetch_tables(sh, p, t.tile);
     // the solve has the final status: repeated ids take the bit-slice ranks
     const bool by_tokens = sh.K >= 4 && !(p.status[0] & MOONEP_STATUS_REPEAT_ID);
     zero_pos(sh, s_pos);
@@ -1231,6 +1247,174 @@ void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     plan_tails(sh, p, tb.upre);
 }
 
+// ---------------------------------------------------------------- k_assign
+// Two 16-wave workgroups per CU need eight waves per SIMD; the attribute makes the
+// compiler budget scalar registers for that (the plan pointers would otherwise
+// hold enough of them to allow only one).
+__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
+    extern __shared__ int32_t smem[];
+    const Tile t = tile_of(sh, blockIdx.x);
+    // loads first, all in flight: this wave's ids, then the tables, which are
+    // only needed once the ranks are taken
+    int idv[kChunks];
+    load_ids(sh, ids, t, idv);
+    const TableRegs regs = fetch_tables(sh, p, t.tile, true);
+    assign_tile(sh, p, t, idv, regs, smem);
+}
+
+// ---------------------------------------------------------------- k_plan_fused
+// The plan in two launches, for problems with few tiles (the decode shape):
+// after k_count, one 1024-thread workgroup per tile
+//   1. sums every tile's counts: T, and the counts of the tiles before its own
+//      (its tile base), threads split as (tile group, expert) and the group
+//      partials added in LDS;
+//   2. runs the solve itself -- every workgroup the same deterministic solve on
+//      the same T, so every workgroup writes the same values to the same plan
+//      entries, and reads back only what it wrote itself (a workgroup barrier
+//      makes its own global writes visible to all its threads);
+//   3. assigns its tile as k_assign does.
+// No workgroup waits for another, so nothing depends on which workgroups are
+// resident at once. The cost is the redundant solve and the count reads, both
+// small at the shapes that take this path (n_tiles * E bounded by kFusedMaxCounts).
+// Te = T of expert threadIdx.x and base = its count in tiles before `tile` (both
+// 0 beyond E), from the 16-bit counts k_count<..., true> wrote; s_part holds
+// gather_part_bytes(). A load takes V consecutive counts: 8 (16 bytes) when
+// E % 8 == 0, 2 when E is even, else 1 (rows of E counts are then aligned to the
+// load). Threads split as (tile group, column of V experts): group g of `groups`
+// takes tiles g, g + groups, ..., each thread keeping U loads in flight; the
+// group partials are added in LDS.
+constexpr int kGatherUnroll = 16;
+
+// Counts per load: 8 (16 bytes) when E % 8 == 0, 2 when E is even, else 1.
+__host__ __device__ inline int gather_width(int E) { return (E & 7) == 0 ? 8 : (E & 1) == 0 ? 2 : 1; }
+
+// Tile groups of the gather: as many as the threads allow, but no more than one
+// batch of `unroll` loads per thread needs (the partials are added serially).
+__host__ __device__ inline int gather_groups(int n_tiles, int cols, int unroll) {
+    const int most = kAssignThreads / cols;  // >= 1: cols <= E <= kAssignThreads
+    const int need = (n_tiles + unroll - 1) / unroll;
+    const int g = most < need ? most : need;
+    return g > 1 ? g : 1;
+}
+
+// Unroll of the gather in each form of the fused kernel (the bounded solve leaves
+// fewer registers to hold loads in flight) and the ints of its LDS partials.
+template <bool BOUNDED>
+constexpr int gather_unroll() { return BOUNDED ? kGatherUnroll / 2 : kGatherUnroll; }
+
+inline size_t gather_part_bytes(const PlanShape &sh, bool bounded) {
+    const int u = bounded ? gather_unroll<true>() : gather_unroll<false>();
+    return sizeof(int32_t) * 2 * (size_t)sh.E *
+           gather_groups(sh.n_tiles, sh.E / gather_width(sh.E), u);
+}
+
+template <int V>
+struct Counts16;
+template <>
+struct Counts16<8> {
+    typedef uint16_t type __attribute__((ext_vector_type(8)));
+    __device__ static int at(const type &x, int v) { return x[v]; }
+};
+template <>
+struct Counts16<2> {
+    typedef uint16_t type __attribute__((ext_vector_type(2)));
+    __device__ static int at(const type &x, int v) { return x[v]; }
+};
+template <>
+struct Counts16<1> {
+    typedef uint16_t type;
+    __device__ static int at(const type &x, int) { return x; }
+};
+
+template <int V, int U>
+__device__ __forceinline__ void gather_cols(const PlanShape &sh, const PlanPtrs &p, int tile,
+                                            int *s_part) {
+    typedef typename Counts16<V>::type vec_t;
+    const int tid = threadIdx.x;
+    const int cols = sh.E / V;
+    const int groups = gather_groups(sh.n_tiles, cols, U);
+    const int g = tid / cols, c = tid - g * cols;
+    if (g >= groups) return;
+    int sum[V], pre[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) sum[v] = pre[v] = 0;
+    const vec_t *col = reinterpret_cast<const vec_t *>(p.tile_counts) + c;
+    // one batch of loads from tiles u0, u0 + groups, ...; the first batch is
+    // straight-line code, so that its loads issue together with the caller's
+    // earlier ones (a loop header makes the compiler wait for those first)
+    auto batch = [&](int u0) {
+        vec_t x[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int u = u0 + j * groups;
+            x[j] = u < sh.n_tiles ? col[(int64_t)u * cols] : vec_t{};
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool before = u0 + j * groups < tile;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int n = Counts16<V>::at(x[j], v);
+                sum[v] += n;
+                pre[v] += before ? n : 0;
+            }
+        }
+    };
+    batch(g);
+    for (int u0 = g + groups * U; u0 < sh.n_tiles; u0 += groups * U) batch(u0);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        s_part[g * sh.E + c * V + v] = sum[v];
+        s_part[(groups + g) * sh.E + c * V + v] = pre[v];
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void gather_counts(const PlanShape &sh, const PlanPtrs &p, int tile,
+                                              int &Te, int &base, int *s_part) {
+    const int tid = threadIdx.x;
+    const int V = gather_width(sh.E);
+    if (V == 8) gather_cols<8, U>(sh, p, tile, s_part);
+    else if (V == 2) gather_cols<2, U>(sh, p, tile, s_part);
+    else gather_cols<1, U>(sh, p, tile, s_part);
+    const int groups = gather_groups(sh.n_tiles, sh.E / V, U);
+    __syncthreads();
+    Te = 0;
+    base = 0;
+    if (tid < sh.E) {
+        for (int q = 0; q < groups; ++q) {
+            Te += s_part[q * sh.E + tid];
+            base += s_part[(groups + q) * sh.E + tid];
+        }
+    }
+    __syncthreads();  // s_part is the solve's LDS next
+}
+
+template <bool BOUNDED>
+__global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__restrict__ ids,
+                                                               PlanShape sh, PlanPtrs p) {
+    extern __shared__ int32_t smem[];
+    const int tid = threadIdx.x;
+    const Tile t = tile_of(sh, blockIdx.x);
+    // the tiles' status words and counts first, so that they share one round
+    // trip; this tile's ids are loaded after the solve, together with the tables
+    // (keeping them in registers across the solve would crowd it)
+    int st = tid < sh.n_tiles ? p.tile_status[tid] : 0;
+    int Te, base;
+    gather_counts<gather_unroll<BOUNDED>()>(sh, p, t.tile, Te, base, smem);
+    for (int u = tid + kAssignThreads; u < sh.n_tiles; u += kAssignThreads) st |= p.tile_status[u];
+    if (blockIdx.x == 0 && tid < sh.E) p.T[tid] = Te;
+    if constexpr (BOUNDED) solve_bounded(sh, p, smem, Te, st);
+    else solve_waterfill(sh, p, smem, Te, st);
+    __syncthreads();  // this workgroup's plan writes are visible to all its threads
+    int idv[kChunks];
+    load_ids(sh, ids, t, idv);
+    TableRegs regs = fetch_tables(sh, p, t.tile, false);
+    regs.tbase = base;
+    assign_tile(sh, p, t, idv, regs, smem);
+}
+
 hipError_t allow_lds(const void *kernel, size_t lds) {
     if (lds <= 65536) return hipSuccess;  // within the default dynamic LDS limit of a launch
     return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1241,9 +1425,15 @@ hipError_t allow_lds(const void *kernel, size_t lds) {
 hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &p, bool bounded,
                        hipStream_t st) {
     const dim3 tiles(sh.n_tiles);
-#define MOONEP_COUNT(KM)                                                                    \
-    hipLaunchKernelGGL(k_count<KM>, tiles, dim3(kPlanThreads), 0, st, ids, sh, p.tile_counts, \
-                       p.tile_status)
+#define MOONEP_COUNT(KM)                                                                      \
+    do {                                                                                      \
+        if (sh.launches == 2)                                                                 \
+            hipLaunchKernelGGL((k_count<KM, true>), tiles, dim3(kPlanThreads), 0, st, ids,    \
+                               sh, p.tile_counts, p.tile_status);                             \
+        else                                                                                  \
+            hipLaunchKernelGGL((k_count<KM, false>), tiles, dim3(kPlanThreads), 0, st, ids,   \
+                               sh, p.tile_counts, p.tile_status);                             \
+    } while (0)
     if (sh.K <= 1) MOONEP_COUNT(1);
     else if (sh.K <= 2) MOONEP_COUNT(2);
     else if (sh.K <= 4) MOONEP_COUNT(4);
@@ -1252,6 +1442,21 @@ hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &
     else if (sh.K <= 32) MOONEP_COUNT(32);
     else MOONEP_COUNT(64);
 #undef MOONEP_COUNT
+    if (sh.launches == 2) {
+        // the gather's partials come first, then the solve's LDS, then assign's
+        size_t lds = solve_lds_bytes(sh, bounded);
+        lds = lds > assign_lds_bytes(sh) ? lds : assign_lds_bytes(sh);
+        const size_t part = gather_part_bytes(sh, bounded);
+        lds = lds > part ? lds : part;
+        const void *k = bounded ? (const void *)k_plan_fused<true> : (const void *)k_plan_fused<false>;
+        hipError_t e = allow_lds(k, lds);
+        if (e != hipSuccess) return e;
+        if (bounded)
+            hipLaunchKernelGGL(k_plan_fused<true>, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
+        else
+            hipLaunchKernelGGL(k_plan_fused<false>, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_scan, dim3((sh.E + 63) / 64), dim3(kScanThreads), 0, st, sh,
                        p.tile_counts, p.T);
     const size_t slds = solve_lds_bytes(sh, bounded);
