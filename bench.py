@@ -347,7 +347,8 @@ def ceilings(wl, buf, stream, reps):
     """Practical HBM ceilings on the receive buffer itself (the 30 GB that
     dispatch writes and combine reads at K3): plain sequential reads, writes and
     copies (first half into second half) with this library's streaming kernels in
-    both launch shapes (one resident grid; one workgroup per 16 KiB), and torch's
+    both launch shapes (one resident grid; one workgroup per 16 KiB, and for
+    writes also per 4 KiB), and torch's
     fill_ (the runtime's memset kernel) and copy_. GB/s of bytes moved (read +
     written), median of `reps` after one warm-up. `read`, `write` and `copy` are
     the best of each kind. The receive buffer is overwritten."""
@@ -381,6 +382,7 @@ def ceilings(wl, buf, stream, reps):
         "read_16k": timed(lambda: ts.stream_read(flat[:n], sink, chunk, stream), n),
         "write_grid": timed(lambda: ts.stream_write(flat[:n], 0, 0, stream), n),
         "write_16k": timed(lambda: ts.stream_write(flat[:n], 0, chunk, stream), n),
+        "write_4k": timed(lambda: ts.stream_write(flat[:n], 0, 4096, stream), n),
         "torch_fill": timed(lambda: flat[:n].fill_(0), n),
         "copy_grid": timed(lambda: ts.stream_copy(b, a, 0, stream), 2 * half),
         "copy_16k": timed(lambda: ts.stream_copy(b, a, chunk, stream), 2 * half),
@@ -388,6 +390,11 @@ def ceilings(wl, buf, stream, reps):
     }
     out = {kind: max(v for k, v in runs.items() if kind in k) for kind in ("read", "write", "copy")}
     out["write"] = max(out["write"], runs["torch_fill"])
+    # A write stream whose concurrent stores lie far apart (the resident grid
+    # walking the buffer) slows down at some physical placements of the buffer,
+    # as dispatch does; one whose stores lie in adjacent 4 KiB pieces does not.
+    # Their ratio tells which placement this process's receive buffer got.
+    out["placement_write_ratio"] = round(runs["write_grid"] / runs["write_4k"], 3)
     out.update({"runs": runs, "bytes": n, "unit": "GB/s", "reps": reps,
                 "kernels": "moonep_stream_read / _write / _copy (include/moonep_stream.h): 16-byte "
                            "accesses, non-temporal loads; torch_fill = fill_(0), torch_copy = copy_"})
