@@ -89,6 +89,12 @@ SMALL = [
     # placement's (rows, id) keys no longer pack into one word, and it takes its
     # three-reduction path; two overflowing experts, pieces on three ranks
     _wl("big_counts", 4, 8, 2, 600_000, 2, 8, W.BF16, 5.0),
+    # more than 64 overflowing experts (103, 206 and 408 at seed 3): the bounded
+    # placement holds them in 2, 4 and 8 registers per lane and searches them
+    # with reductions; up to 64 it keeps them sorted across one wave instead
+    _wl("over_103", 512, 1024, 4, 8, 2, 64, W.BF16, 1.0),
+    _wl("over_206", 512, 1024, 8, 8, 2, 64, W.BF16, 0.3),
+    _wl("over_408", 1024, 1024, 2, 4, 2, 64, W.BF16, 0.0),
 ]
 
 
@@ -306,6 +312,24 @@ def test_extreme_skew_and_balance(td, bounded):
     w = np.full(ids.size, 0.25, np.float32)
     g = _full_case(td, wl, ids, w, 2, bounded)
     assert int(g["n_dup"].sum()) == 0 and float(g["maxvio"][0]) == 0.0
+
+
+@PLANS
+def test_overflows_past_512(td, bounded):
+    # one expert per rank; 700 experts get S*K + 1 entries and the other 324
+    # make up the total: 700 one-row overflows (16 registers per lane in the
+    # bounded placement) onto 324 ranks short by 2 or 3 rows
+    wl = _wl("over_700", 1024, 1024, 2, 4, 4, 64, W.BF16, 0.0)
+    counts = np.concatenate([np.full(700, wl.SK + 1), np.full(272, wl.SK - 2),
+                             np.full(52, wl.SK - 3)]).astype(np.int64)
+    assert counts.sum() == wl.n_ent
+    flat = np.repeat(np.arange(wl.E, dtype=np.int32), counts)
+    # token t takes entries t and t + n_tok of the sorted list: two distinct experts
+    ids = np.stack([flat[:wl.n_tok], flat[wl.n_tok:]], axis=1)
+    ids = ids[np.random.default_rng(5).permutation(wl.n_tok)].reshape(-1)
+    w = np.full(ids.size, 0.5, np.float32)
+    g = _full_case(td, wl, ids, w, 4, bounded)
+    assert int((g["O"] > 0).sum()) == 700 and int(g["n_list"][0]) >= 700
 
 
 def test_identity_expert_mean_returns_hidden(td):

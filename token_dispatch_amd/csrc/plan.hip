@@ -449,8 +449,8 @@ inline size_t solve_lds_bytes(const PlanShape &sh, bool bounded) {
 
 // ---------------------------------------------------------------- water-fill solve
 // One 1024-thread workgroup; smem holds wf_lds() ints.
-__device__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p, int32_t *smem, int Te,
-                                int st) {
+__device__ __forceinline__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p,
+                                                int32_t *smem, int Te, int st) {
     WfLds L;
     wf_lds(sh.E, sh.R, sh.pcap, smem, &L);
     int *const s_T = L.T, *const s_cum = L.cum, *const s_ovpre = L.ovpre, *const s_ovp = L.ovp;
@@ -612,7 +612,8 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
 // overflows with that many rows left, so one placement step is a few wave-wide
 // maximum reductions over the overflows, which wave 0 holds in registers
 // (kMaxE / 64 per lane): two when (rows, id) packs into one 31-bit key, three
-// otherwise.
+// otherwise. Up to 64 overflows with packed keys take place_pieces_sorted, where
+// a step is a few ballots over the overflows kept in order.
 constexpr int kItemsPerLane = kMaxE / 64;
 
 // Maximum over the 64 lanes, in every lane: DPP shifts inside each 16-lane row,
@@ -736,9 +737,196 @@ __device__ __forceinline__ int place_pieces(const PlaceArgs &a, bool packed) {
     return packed ? place_pieces<NS, true>(a) : place_pieces<NS, false>(a);
 }
 
+// v_writelane_b32: reg with lane `lane` set to val (both wave-uniform).
+__device__ int amdgcn_writelane(int val, int lane, int reg) __asm("llvm.amdgcn.writelane.i32");
+
+// The same placement for at most 64 overflows whose rows fit 21 bits, with the
+// overflows kept sorted across the wave instead of searched: lane p holds the
+// overflow at position p of the order (rows left descending, then id ascending)
+// as the key ((rows - 1) << 10) | (kMaxE - 1 - id), and a wave-uniform mask has
+// a bit per lane whose overflow still has rows. Every rule then reads the first
+// (or last) set bit of a ballot:
+//   largest that fits whole  first live lane with key < room << 10
+//   largest                  first live lane
+//   smallest that fills      the last live lane with key >= (room - 1) << 10
+//                            has the fewest rows; the first live lane with those
+//                            rows has the lowest id among them
+// A piece that cuts an overflow (always a rank's last) moves its key down past
+// the live keys that are now larger. One step is a chain of scalar work around
+// one ballot and one lane read; the pieces are recorded in three registers
+// (lane = piece mod 64: the key the piece was cut from, the rank's room before
+// it and the rank's place in fill order) and the ranks in three more (lane =
+// place mod 64), each written to LDS 64 at a time.
+struct PieceRegs {
+    int key, room, bin;
+};
+
+__device__ __forceinline__ void flush_pieces(const PlaceArgs &a, const PieceRegs &g, int base,
+                                             int count) {
+    const int lane = lane_id();
+    if (lane < count) {
+        const int q = base + lane;
+        const int v = (g.key >> 10) + 1, e = (kMaxE - 1) - (g.key & (kMaxE - 1));
+        a.s_pe[q] = e;
+        a.s_pr[q] = a.s_bin[g.bin];
+        a.s_pstart[q] = a.s_binK[g.bin] + (a.s_binD[g.bin] - g.room);
+        a.s_pcnt[q] = min(v, g.room);
+        a.s_pjj[q] = a.s_ov[e] - v;  // first overflow row of the piece
+    }
+}
+
+// all 64 records, pieces base .. base + 63
+__device__ __forceinline__ void flush_pieces64(const PlaceArgs &a, const PieceRegs &g, int base) {
+    const int q = base + lane_id();
+    const int v = (g.key >> 10) + 1, e = (kMaxE - 1) - (g.key & (kMaxE - 1));
+    a.s_pe[q] = e;
+    a.s_pr[q] = a.s_bin[g.bin];
+    a.s_pstart[q] = a.s_binK[g.bin] + (a.s_binD[g.bin] - g.room);
+    a.s_pcnt[q] = min(v, g.room);
+    a.s_pjj[q] = a.s_ov[e] - v;
+}
+
+struct BinRegs {
+    int r, D, first, nd, fill;  // lane j: rank and deficit of place base + j; its results
+};
+
+__device__ __forceinline__ void flush_bins(const PlaceArgs &a, const BinRegs &b, int count) {
+    if (lane_id() < count) {
+        a.s_first[b.r] = b.first;
+        a.s_nd[b.r] = b.nd;
+        a.s_fill[b.r] = b.fill;
+    }
+}
+
+__device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
+    constexpr int kRowsCap = 1 << 21;  // rows of every overflow are below this
+    const int lane = lane_id();
+    const int n0 = __builtin_amdgcn_readfirstlane(a.n_items);
+    const int nb = __builtin_amdgcn_readfirstlane(a.n_bins);
+    const int fit_pieces = __builtin_amdgcn_readfirstlane(a.B - 1);
+    int key = 0;
+    if (lane < n0) {
+        const int id = a.s_xl[lane];
+        key = ((a.s_ov[id] - 1) << 10) | (kMaxE - 1 - id);
+    }
+    // position of each key in descending order (the keys are distinct); empty
+    // lanes keep their own
+    int pos = lane;
+    if (lane < n0) {
+        pos = 0;
+        for (int j = 0; j < n0; ++j) pos += __builtin_amdgcn_readlane(key, j) > key ? 1 : 0;
+    }
+    key = __builtin_amdgcn_ds_permute(pos << 2, key);
+    uint64_t live = n0 >= 64 ? ~0ull : (1ull << n0) - 1;
+
+    // No check against the piece tables' room: every piece but a rank's last
+    // places an overflow whole, so pieces <= overflows + ranks - 1 < pcap.
+    PieceRegs g{0, 0, 0};
+    BinRegs b{0, 0, 0, 0, 0};
+    int np = 0, bi = 0;
+    while (bi < nb && live != 0) {
+        const int bl = bi & 63;
+        if (bl == 0) {
+            const int j = bi + lane;
+            b.r = j < nb ? a.s_bin[j] : 0;
+            b.D = j < nb ? a.s_binD[j] : 0;
+        }
+        const int D = __builtin_amdgcn_readlane(b.D, bl);
+        int room = D, used = 0, cut = -1;  // cut: lane of an overflow the rank's last piece cuts
+        const int first = np;
+        // A step writes its piece at lane np % 64 of the records and counts it
+        // only if the piece places its overflow whole; a piece that cuts is
+        // written again, and counted, below. Each loop tests its exit at the
+        // bottom only; a step after the last live overflow is gone (bit 63 of
+        // an empty mask) counts nothing.
+        auto step = [&](int L, int k, bool whole) {
+            const int slot = np & 63;
+            g.key = amdgcn_writelane(k, slot, g.key);
+            g.room = amdgcn_writelane(room, slot, g.room);
+            g.bin = amdgcn_writelane(bi, slot, g.bin);
+            if (whole) {
+                ++np;
+                ++used;
+                room -= (k >> 10) + 1;
+                live &= ~(1ull << L);
+                if ((np & 63) == 0) flush_pieces64(a, g, np - 64);
+            }
+        };
+        constexpr uint64_t kTop = 1ull << 63;
+        // pieces 1 .. B-1: the largest overflow that fits whole; if none fits
+        // (and rows are left), a piece of the largest
+        if (used < fit_pieces) {
+            bool fits;
+            int L;
+            do {
+                const int rc = min(room, kRowsCap);
+                const uint64_t m =
+                    __builtin_amdgcn_ballot_w64((unsigned)key < ((unsigned)rc << 10)) & live;
+                fits = m != 0;
+                L = __builtin_ctzll((fits ? m : live) | kTop);
+                step(L, __builtin_amdgcn_readlane(key, L), fits);
+            } while (fits && used < fit_pieces);
+            if (!fits && room > 0 && live != 0) cut = L;
+        }
+        // then the smallest overflow that fills the room (lowest id among those
+        // rows), or if none is that large the largest whole
+        if (cut < 0 && room > 0 && live != 0) {
+            bool whole;
+            int L;
+            do {
+                const int rc = min(room, kRowsCap);
+                const uint64_t ge = __builtin_amdgcn_ballot_w64(key >= ((rc - 1) << 10)) & live;
+                const int h = 63 - __builtin_clzll(ge | 1);
+                const int kh = __builtin_amdgcn_readlane(key, h) & ~(kMaxE - 1);
+                const uint64_t eq =
+                    __builtin_amdgcn_ballot_w64((unsigned)(key - kh) < (unsigned)kMaxE) & live;
+                L = __builtin_ctzll((ge != 0 ? eq : live) | kTop);
+                const int k = __builtin_amdgcn_readlane(key, L);
+                whole = live != 0 && (k >> 10) + 1 <= room;
+                step(L, k, whole);
+            } while (whole && room > 0);
+            if (!whole && live != 0) cut = L;
+        }
+        if (cut >= 0) {
+            // the overflow keeps rows: its key drops below the live keys of the
+            // lanes up to A, which move up one lane with their bits
+            const int L = cut;
+            const int k = __builtin_amdgcn_readlane(key, L);
+            const int slot = np & 63;
+            g.key = amdgcn_writelane(k, slot, g.key);
+            g.room = amdgcn_writelane(room, slot, g.room);
+            g.bin = amdgcn_writelane(bi, slot, g.bin);
+            ++np;
+            ++used;
+            if ((np & 63) == 0) flush_pieces64(a, g, np - 64);
+            const int k2 = k - (room << 10);
+            room = 0;
+            const uint64_t gt = __builtin_amdgcn_ballot_w64(key > k2) & live & ~(1ull << L);
+            const int A = gt != 0 ? 63 - __builtin_clzll(gt) : -1;
+            if (A > L) {
+                const int src = lane >= L && lane < A ? lane + 1 : lane;
+                key = __builtin_amdgcn_ds_bpermute(src << 2, key);
+                key = amdgcn_writelane(k2, A, key);
+                const uint64_t span = ((2ull << A) - 1) & ~((1ull << L) - 1);  // bits L..A
+                live = (live & ~span) | ((live >> 1) & span) | (1ull << A);
+            } else {
+                key = amdgcn_writelane(k2, L, key);
+            }
+        }
+        b.first = amdgcn_writelane(first, bl, b.first);
+        b.nd = amdgcn_writelane(used, bl, b.nd);
+        b.fill = amdgcn_writelane(D - room, bl, b.fill);
+        ++bi;
+        if ((bi & 63) == 0) flush_bins(a, b, 64);
+    }
+    if ((bi & 63) != 0) flush_bins(a, b, bi & 63);
+    if ((np & 63) != 0) flush_pieces(a, g, np & ~63, np & 63);
+    return np;
+}
+
 // One 1024-thread workgroup; smem holds bd_lds() ints.
-__device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *smem, int Te,
-                              int st) {
+__device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p,
+                                              int32_t *smem, int Te, int st) {
     BdLds L;
     bd_lds(sh.E, sh.R, sh.pcap, smem, &L);
     uint64_t *const s_bkey = L.bkey;
@@ -816,7 +1004,8 @@ __device__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p, int32_t *s
         const int nslots = (n_items + 63) >> 6;
         const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
         int np;
-        if (nslots <= 1) np = place_pieces<1>(a, packed);
+        if (nslots <= 1 && packed) np = place_pieces_sorted(a);
+        else if (nslots <= 1) np = place_pieces<1, false>(a);
         else if (nslots <= 2) np = place_pieces<2>(a, packed);
         else if (nslots <= 4) np = place_pieces<4>(a, packed);
         else if (nslots <= 8) np = place_pieces<8>(a, packed);
