@@ -752,7 +752,8 @@ __device__ int amdgcn_writelane(int val, int lane, int reg) __asm("llvm.amdgcn.w
 //                            has the fewest rows; the first live lane with those
 //                            rows has the lowest id among them
 // A piece that cuts an overflow (always a rank's last) moves its key down past
-// the live keys that are now larger. One step is a chain of scalar work around
+// the live keys that are now larger, the keys between moving up one lane (a
+// whole-wave DPP shift). One step is a chain of scalar work around
 // one ballot and one lane read; the pieces are recorded in three registers
 // (lane = piece mod 64: the key the piece was cut from, the rank's room before
 // it and the rank's place in fill order) and the ranks in three more (lane =
@@ -904,8 +905,9 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
             const uint64_t gt = __builtin_amdgcn_ballot_w64(key > k2) & live & ~(1ull << L);
             const int A = gt != 0 ? 63 - __builtin_clzll(gt) : -1;
             if (A > L) {
-                const int src = lane >= L && lane < A ? lane + 1 : lane;
-                key = __builtin_amdgcn_ds_bpermute(src << 2, key);
+                // DPP wave_shl:1: lane i reads lane i + 1
+                const int next = __builtin_amdgcn_update_dpp(key, key, 0x130, 0xf, 0xf, false);
+                key = lane >= L && lane < A ? next : key;
                 key = amdgcn_writelane(k2, A, key);
                 const uint64_t span = ((2ull << A) - 1) & ~((1ull << L) - 1);  // bits L..A
                 live = (live & ~span) | ((live >> 1) & span) | (1ull << A);
