@@ -258,8 +258,13 @@ __global__ __launch_bounds__(kMoveThreads) void k_reduce(
     }
 }
 
-// Grid of the fixed-size copy kernels: enough workgroups to fill 256 CUs.
-constexpr int kCopyGrid = 256 * 8;
+// Grids of the fixed-size kernels, in workgroups per CU of the 256. Replicate
+// streams best with two (one process, same buffers, medians of five: K3 0.844
+// against 0.890 ms with eight, decode 0.693 against 0.724, zipf 0.416 against
+// 0.420), reduce with six (K3 2.314 against 2.366 ms, decode 2.022 against
+// 2.081); four or fewer made reduce slower, one or three made replicate slower.
+constexpr int kRepGrid = 256 * 2;
+constexpr int kRedGrid = 256 * 6;
 
 }  // namespace
 
@@ -388,7 +393,7 @@ hipError_t launch_replicate(const PlanShape &sh, const PlanPtrs &p, const void *
     if (sh.B == 0) return hipSuccess;
     const int64_t chunks = block_bytes / 16;
     const int64_t ips = (chunks + kCopyChunks - 1) / kCopyChunks;
-    hipLaunchKernelGGL(k_replicate, dim3(kCopyGrid), dim3(kMoveThreads), 0, st,
+    hipLaunchKernelGGL(k_replicate, dim3(kRepGrid), dim3(kMoveThreads), 0, st,
                        static_cast<const v4u *>(expert_w), static_cast<v4u *>(dup_w),
                        p.mat_pre, p.dup_expert, sh.R, sh.E, sh.B, sh.dcap, chunks, ips);
     return hipGetLastError();
@@ -399,7 +404,7 @@ hipError_t launch_reduce(const PlanShape &sh, const PlanPtrs &p, const float *du
     if (sh.B == 0) return hipSuccess;
     const int64_t n4 = block_elems / 4;
     const int64_t ipe = (n4 + kRedVecs - 1) / kRedVecs;
-    hipLaunchKernelGGL(k_reduce, dim3(kCopyGrid), dim3(kMoveThreads), 0, st,
+    hipLaunchKernelGGL(k_reduce, dim3(kRedGrid), dim3(kMoveThreads), 0, st,
                        reinterpret_cast<const float4 *>(dup_grads),
                        reinterpret_cast<float4 *>(home_grads), p.xlist, p.n_x, p.dup_ptr,
                        p.list_rank, p.list_b, sh.R, sh.B, n4, ipe);
