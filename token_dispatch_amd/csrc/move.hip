@@ -120,18 +120,19 @@ __device__ __forceinline__ void combine_rows(const v4u *__restrict__ y, int my_d
 }
 
 // One wave per work item (token, row segment) of the launch's range [i_lo, i_hi).
+// Rows of at most 4 chunks per lane are held to 64 VGPRs (8 waves per SIMD, 61
+// without spills instead of 71 and 7 waves): uniform's 4 KiB rows then take 4
+// launches per call instead of 5, and dispatch + combine went from 0.443 to
+// 0.437 ms there (one process, same buffers).
 // UNIT_W: every weight is 1 and w is not read; fma(1, x, acc) is the binary32
 // sum acc + x, which makes this the backward of dispatch. Rows are read through
 // a buffer resource when they are shorter than about 2^31 bytes (5.26 -> 5.19 ms
 // at K3, from the address arithmetic it saves), else with global loads.
 template <int CPL, bool IN_BF16, bool OUT_BF16, bool UNIT_W>
-__global__ __launch_bounds__(kMoveThreads) void k_combine(const v4u *__restrict__ y,
-                                                          const float *__restrict__ w,
-                                                          const int32_t *__restrict__ dst,
-                                                          void *__restrict__ out,
-                                                          int64_t i_lo, int64_t i_hi,
-                                                          int32_t segs, int32_t C, int32_t K,
-                                                          int64_t n_slots) {
+__global__ __launch_bounds__(kMoveThreads) __attribute__((amdgpu_waves_per_eu(CPL <= 4 ? 8 : 1)))
+void k_combine(const v4u *__restrict__ y, const float *__restrict__ w,
+               const int32_t *__restrict__ dst, void *__restrict__ out, int64_t i_lo,
+               int64_t i_hi, int32_t segs, int32_t C, int32_t K, int64_t n_slots) {
     using Ch = Chunk<IN_BF16>;
     constexpr int N = Ch::N;
     const int lane = lane_id();

@@ -67,19 +67,29 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = max(x, __shfl_xor(x, d, 64));
-    return x;
+// Maximum over the 64 lanes, in every lane: DPP shifts inside each 16-lane row,
+// then rows 0 -> 1 and 1 -> 2,3 broadcasts (lane 63 ends with the maximum).
+__device__ __forceinline__ int wave_reduce_max(int x) {
+    constexpr int kLo = -2147483647 - 1;
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(x, 63);
 }
 
 // Exclusive scans of NV values per thread over the 1024-thread workgroup, all
-// in one pass (three barriers). s_w needs (16 + 1) * NV ints. Every thread must
-// call it; tot[i] receives the total of value i.
+// in one pass (two barriers): each wave scans itself, publishes its total, then
+// scans the 16 totals itself. s_w needs 16 * NV ints. Every thread must call it;
+// tot[i] receives the total of value i. LDS written before the call is visible
+// to every thread after it.
 template <int NV>
 __device__ void block_excl_scan(const int *v, int *res, int *tot, int *s_w) {
     constexpr int NW = kSolveThreads / 64;
-    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     int inc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) inc[i] = wave_incl_scan(v[i]);
@@ -88,22 +98,14 @@ __device__ void block_excl_scan(const int *v, int *res, int *tot, int *s_w) {
         for (int i = 0; i < NV; ++i) s_w[i * NW + w] = inc[i];
     }
     __syncthreads();
-    if (w == 0) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int t = lane < NW ? s_w[i * NW + lane] : 0;
-            const int ti = wave_incl_scan(t);
-            if (lane < NW) s_w[i * NW + lane] = ti - t;
-            if (lane == NW - 1) s_w[NV * NW + i] = ti;
-        }
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        res[i] = inc[i] - v[i] + s_w[i * NW + w];
-        tot[i] = s_w[NV * NW + i];
+        const int ti = wave_incl_scan(lane < NW ? s_w[i * NW + lane] : 0);
+        const int before = w == 0 ? 0 : __builtin_amdgcn_readlane(ti, w - 1);
+        res[i] = inc[i] - v[i] + before;
+        tot[i] = __builtin_amdgcn_readlane(ti, NW - 1);
     }
-    __syncthreads();
+    __syncthreads();  // s_w is free for the next scan
 }
 
 // First index i in [0, n) with a[i] > x (n if none).
@@ -318,7 +320,7 @@ __device__ Head solve_head(const PlanShape &sh, const PlanPtrs &p, int Te, int s
     __syncthreads();
     if (st) atomicOr(s_status, st);
     {
-        const int m = wave_max(h.Te);
+        const int m = wave_reduce_max(h.Te);
         if (lane == 0) atomicMax(s_maxT, m);
     }
     // home offsets and load; expert e lives on rank e / G
@@ -616,19 +618,6 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs 
 // a step is a few ballots over the overflows kept in order.
 constexpr int kItemsPerLane = kMaxE / 64;
 
-// Maximum over the 64 lanes, in every lane: DPP shifts inside each 16-lane row,
-// then rows 0 -> 1 and 1 -> 2,3 broadcasts (lane 63 ends with the maximum).
-__device__ __forceinline__ int wave_reduce_max(int x) {
-    constexpr int kLo = -2147483647 - 1;
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x111, 0xf, 0xf, false));  // row_shr:1
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x112, 0xf, 0xf, false));  // row_shr:2
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x114, 0xf, 0xf, false));  // row_shr:4
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x118, 0xf, 0xf, false));  // row_shr:8
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
-    x = max(x, __builtin_amdgcn_update_dpp(kLo, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return __builtin_amdgcn_readlane(x, 63);
-}
-
 struct PlaceArgs {
     int n_items, n_bins, B, cap;
     const int *s_xl, *s_ov;
@@ -833,13 +822,14 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
             b.D = j < nb ? a.s_binD[j] : 0;
         }
         const int D = __builtin_amdgcn_readlane(b.D, bl);
-        int room = D, used = 0, cut = -1;  // cut: lane of an overflow the rank's last piece cuts
+        int room = D, used = 0;
+        int cut = -1, ck = 0;  // lane and key of an overflow the rank's last piece cuts
         const int first = np;
         // A step writes its piece at lane np % 64 of the records and counts it
         // only if the piece places its overflow whole; a piece that cuts is
-        // written again, and counted, below. Each loop tests its exit at the
-        // bottom only; a step after the last live overflow is gone (bit 63 of
-        // an empty mask) counts nothing.
+        // counted below, its record already written by the step that chose it.
+        // Each loop tests its exit at the bottom only; a step after the last
+        // live overflow is gone (bit 63 of an empty mask) counts nothing.
         auto step = [&](int L, int k, bool whole) {
             const int slot = np & 63;
             g.key = amdgcn_writelane(k, slot, g.key);
@@ -858,22 +848,26 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
         // (and rows are left), a piece of the largest
         if (used < fit_pieces) {
             bool fits;
-            int L;
+            int L, k;
             do {
                 const int rc = min(room, kRowsCap);
                 const uint64_t m =
                     __builtin_amdgcn_ballot_w64((unsigned)key < ((unsigned)rc << 10)) & live;
                 fits = m != 0;
                 L = __builtin_ctzll((fits ? m : live) | kTop);
-                step(L, __builtin_amdgcn_readlane(key, L), fits);
+                k = __builtin_amdgcn_readlane(key, L);
+                step(L, k, fits);
             } while (fits && used < fit_pieces);
-            if (!fits && room > 0 && live != 0) cut = L;
+            if (!fits && room > 0 && live != 0) {
+                cut = L;
+                ck = k;
+            }
         }
         // then the smallest overflow that fills the room (lowest id among those
         // rows), or if none is that large the largest whole
         if (cut < 0 && room > 0 && live != 0) {
             bool whole;
-            int L;
+            int L, k;
             do {
                 const int rc = min(room, kRowsCap);
                 const uint64_t ge = __builtin_amdgcn_ballot_w64(key >= ((rc - 1) << 10)) & live;
@@ -882,25 +876,23 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
                 const uint64_t eq =
                     __builtin_amdgcn_ballot_w64((unsigned)(key - kh) < (unsigned)kMaxE) & live;
                 L = __builtin_ctzll((ge != 0 ? eq : live) | kTop);
-                const int k = __builtin_amdgcn_readlane(key, L);
+                k = __builtin_amdgcn_readlane(key, L);
                 whole = live != 0 && (k >> 10) + 1 <= room;
                 step(L, k, whole);
             } while (whole && room > 0);
-            if (!whole && live != 0) cut = L;
+            if (!whole && live != 0) {
+                cut = L;
+                ck = k;
+            }
         }
         if (cut >= 0) {
             // the overflow keeps rows: its key drops below the live keys of the
             // lanes up to A, which move up one lane with their bits
             const int L = cut;
-            const int k = __builtin_amdgcn_readlane(key, L);
-            const int slot = np & 63;
-            g.key = amdgcn_writelane(k, slot, g.key);
-            g.room = amdgcn_writelane(room, slot, g.room);
-            g.bin = amdgcn_writelane(bi, slot, g.bin);
             ++np;
             ++used;
             if ((np & 63) == 0) flush_pieces64(a, g, np - 64);
-            const int k2 = k - (room << 10);
+            const int k2 = ck - (room << 10);
             room = 0;
             const uint64_t gt = __builtin_amdgcn_ballot_w64(key > k2) & live & ~(1ull << L);
             const int A = gt != 0 ? 63 - __builtin_clzll(gt) : -1;
