@@ -511,7 +511,7 @@ __device__ __forceinline__ void solve_waterfill(const PlanShape &sh, const PlanP
             dend = min(s_Dpre[r + 1], totO);
             if (dend > dbeg) k = upper_bound(s_ovp, totNZ + 1, (x & 1) ? dend - 1 : dbeg) - 1;
         }
-        const int k_end = __shfl_xor(k, 1);
+        const int k_end = __builtin_amdgcn_mov_dpp(k, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]: lane ^ 1
         if (r < R && (x & 1) == 0) {
             s_dbeg[r] = dbeg;
             s_dend[r] = dend;
@@ -941,9 +941,12 @@ __device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtr
     if (tid < E) {
         const int r = tid / G;
         int before = 0;  // rows of the rank's experts that come before this one
+        // branch-free and unrolled, so that the LDS reads go out together
+#pragma unroll 8
         for (int e2 = r * G; e2 < (r + 1) * G; ++e2) {
             const int t2 = s_T[e2];
-            before += (t2 > h.Te || (t2 == h.Te && e2 < tid)) ? t2 : 0;
+            const bool ahead = (t2 > h.Te) | ((t2 == h.Te) & (e2 < tid));
+            before += ahead ? t2 : 0;
         }
         ov = min(max(s_O[r] - before, 0), h.Te);
         s_ov[tid] = ov;
