@@ -61,7 +61,8 @@ def algorithmic_bytes(wl, n_mat, n_xm):
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic_k3.json")
 
 # Library kernels behind each C-ABI call (one call may enqueue several launches).
-OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign"),
+OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign",
+                       "k_plan_fused"),
               "replicate": ("k_replicate",),
               "dispatch": ("k_dispatch",), "combine": ("k_combine",), "reduce": ("k_reduce",)}
 # (k_combine also serves the backward of dispatch, so traffic is only summed for
@@ -128,9 +129,9 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, co
 
 # Kernel classes of a counter summary: the library's kernels and the streaming
 # kernels the ceilings are measured with.
-PMC_CLASSES = ("k_count", "k_scan", "k_solve", "k_assign", "k_replicate", "k_dispatch",
-               "k_combine", "k_reduce", "k_bwd_dot", "k_bwd_scatter", "k_stream_read",
-               "k_stream_write", "k_stream_copy")
+PMC_CLASSES = ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_assign", "k_plan_fused",
+               "k_replicate", "k_dispatch", "k_combine", "k_reduce", "k_bwd_dot", "k_bwd_scatter",
+               "k_stream_read", "k_stream_write", "k_stream_copy")
 
 
 def pmc_summary(dirs):

@@ -163,3 +163,21 @@ def test_pmc_summary_by_hand(tmp_path):
     assert rec["rdreq_latency_cycles"] == pytest.approx(75.0)
     assert rec["rdreq_in_flight"] == pytest.approx(7500.0 / 800.0 * 8)
     assert rec["median_us"] == pytest.approx(2.0)
+
+
+def test_every_kernel_is_counted():
+    """Every __global__ kernel of the library sources has a class in the counter
+    summary, and every forward kernel belongs to one call's traffic (the backward
+    kernels are summed only by runs without --with-backward)."""
+    import re
+    names = set()
+    csrc = os.path.join(ROOT, "token_dispatch_amd", "csrc")
+    for f in os.listdir(csrc):
+        if f.endswith(".hip"):
+            text = open(os.path.join(csrc, f)).read()
+            names |= set(re.findall(r"__global__[^;{]*?\bvoid\s+(k_\w+)\s*\(", text))
+    assert {"k_count", "k_plan_fused", "k_solve_bounded", "k_combine", "k_stream_copy"} <= names
+    for n in names:
+        assert n in bench.PMC_CLASSES, n
+        if not n.startswith(("k_bwd", "k_stream")):
+            assert any(n in ks for ks in bench.OP_KERNELS.values()), n
