@@ -332,6 +332,83 @@ def test_overflows_past_512(td, bounded):
     assert int((g["O"] > 0).sum()) == 700 and int(g["n_list"][0]) >= 700
 
 
+def _ids_from_counts(T, n_tok, K, seed):
+    """Router ids with exactly T[e] entries of expert e and K distinct experts per
+    token: the sorted id list is cut into K columns of n_tok (no expert has more
+    than n_tok entries, so a token's K ids come from K different runs)."""
+    T = np.asarray(T, dtype=np.int64)
+    flat = np.repeat(np.arange(T.size, dtype=np.int32), T)
+    assert flat.size == n_tok * K and int(T.max()) <= n_tok
+    ids = flat.reshape(K, n_tok).T.copy()
+    return ids[np.random.default_rng(seed).permutation(n_tok)].reshape(-1)
+
+
+def _balanced_counts(R, G, SK, over, short, seed):
+    """Expert counts for R ranks of G experts: ranks in `over` get extra rows (one
+    list of per-expert extras each), ranks in `short` fewer rows; the rest exactly
+    S*K. Overflows and deficits are placed on random ranks."""
+    T = np.full((R, G), SK // G, dtype=np.int64)
+    T[:, : SK % G] += 1
+    idx = np.random.default_rng(seed).permutation(R)
+    for r, extra in zip(idx[: len(over)], over):
+        T[r, : len(extra)] += np.asarray(extra)
+    for r, d in zip(idx[len(over): len(over) + len(short)], short):
+        left = d
+        for g in range(G):
+            take = min(left, int(T[r, g]))
+            T[r, g] -= take
+            left -= take
+        assert left == 0
+    T = T.reshape(-1)
+    assert T.sum() == R * SK
+    return T
+
+
+def _deficits(total, hi, seed):
+    rng = np.random.default_rng(seed)
+    d = []
+    while sum(d) < total:
+        d.append(min(1 + int(rng.integers(0, hi)), total - sum(d)))
+    return d
+
+
+# Routings built from per-expert counts for the edges of the bounded placement:
+# exactly 64 overflows (every lane of the sorted wave live) and 65 (the register-
+# slot search), ties in rows, B = 1 (no fit-whole pieces), overflows cut over many
+# deficit ranks, and deficits of more than 2^21 rows with every overflow below it.
+def _edge_cases():
+    def rows(over):
+        return sum(sum(x) for x in over)
+    out = []
+    ov = [[1 + (i % 8)] for i in range(64)]
+    out.append(("ov64_unit", 128, 1, 2, 4, 2, [[1]] * 64, [1] * 64))
+    out.append(("ov64_ties", 256, 1, 4, 16, 3, ov, _deficits(rows(ov), 12, 1)))
+    ov65 = ov + [[5]]
+    out.append(("ov65_ties", 256, 1, 4, 16, 3, ov65, _deficits(rows(ov65), 12, 2)))
+    out.append(("ov63_fill_only", 256, 1, 4, 16, 1, ov[:63], _deficits(rows(ov[:63]), 9, 3)))
+    big = [[300], [280], [280], [150]]
+    out.append(("cut_heavy", 256, 1, 4, 64, 4, big, _deficits(rows(big), 9, 4)))
+    mixed = [[500]] + [[10]] * 40 + [[1]] * 20
+    out.append(("one_big", 256, 1, 4, 64, 2, mixed, _deficits(rows(mixed), 16, 5)))
+    SK = (1 << 21) + (1 << 20)
+    q = SK // 4
+    out.append(("room_past_2p21", 2, 4, 1, SK, 2, [[q - 1000, q, q, q - 1000]], [SK - 2000]))
+    return out
+
+
+@PLANS
+@pytest.mark.parametrize("case", _edge_cases(), ids=lambda c: c[0])
+def test_bounded_placement_edges(td, case, bounded):
+    name, R, G, K, S, B, over, short = case
+    wl = _wl(name, R, R * G, K, S, B, 8, W.BF16, 0.0)
+    T = _balanced_counts(R, G, S * K, over, short, 7)
+    ids = _ids_from_counts(T, R * S, K, 8)
+    w = np.full(ids.size, 1.0 / K, np.float32)
+    g = _full_case(td, wl, ids, w, 5, bounded)
+    n_over = len(over) if G == 1 else int((g["O"] > 0).sum())
+    assert int((g["O"] > 0).sum()) == n_over
+
+
 def test_identity_expert_mean_returns_hidden(td):
     """y = recv and w = 1/K with K a power of two: combine gives back hidden bit for bit."""
     wl = _wl("identity", 8, 64, 8, 900, 8, 512, W.BF16, 2.0)
