@@ -6,7 +6,7 @@
 //   grad_w[g,k] = <grad_out[g], y[dst(g,k)]>   k_bwd_dot: pure reads (y once,
 //                 grad_out once per token), one wave per token, non-temporal
 //                 loads; each lane accumulates its elements with fma in eight
-//                 short chains, then a fixed butterfly sums the 64 lanes.
+//                 short chains, then a fixed DPP reduction sums the 64 lanes.
 //   grad_y[dst(g,k)] = w[g,k] * grad_out[g]    k_bwd_scatter: write-heavy like
 //                 dispatch, so it runs the same way: resident-grid launches over
 //                 token chunks, every wave first loads its grad_out row segments,
@@ -25,11 +25,25 @@ namespace {
 
 using namespace rows;
 
-// Sum over the 64 lanes in a fixed butterfly order; every lane gets the sum.
+// v + v moved by DPP control CTRL in the rows ROWS (lanes with no source add +0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf,
+                                                          false));
+}
+
+// Sum over the 64 lanes in a fixed order; every lane gets the sum. DPP moves
+// (no LDS): shifts by 1, 2, 4, 8 inside each 16-lane row, then lane 15 of a row
+// into the next row and lane 31 into the upper two rows, which leaves the sum in
+// lane 63.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
+    x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);  // row_bcast:15
+    x = dpp_add<0x143, 0xc>(x);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // ---------------------------------------------------------------- grad_w
@@ -38,7 +52,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // l, l + 64, ... of each segment and keeps one binary32 accumulator per element
 // position j of a chunk (fma in chunk order), so the eight chains are short and
 // independent; they are summed j = 0..N-1, then over the lanes by a fixed
-// butterfly. ONE_SEG: the whole grad_out row sits in registers (packed), reused
+// DPP reduction. ONE_SEG: the whole grad_out row sits in registers (packed), reused
 // for every k, and the y row of k+1 is loaded while k is summed.
 template <bool BF16, int N>
 struct RowIO;

@@ -6,7 +6,11 @@
 // maxvio = max_e(T_e / Tbar) - 1 ("Why expert parallelism is needed", same page;
 // blog.schoergendorfer.com, "The problem MoonEP targets").
 //
-// Four launches, every grid fixed by the dims alone (no host round trip):
+// Every grid is fixed by the dims alone (no host round trip). The plan runs as
+// four launches, k_count, k_scan, k_solve (or k_solve_bounded), k_assign, or as
+// two: k_count, then k_plan_fused, in which every workgroup gathers all tiles'
+// counts, runs the whole solve itself and assigns its own tile (no hand-over
+// between workgroups); the layout takes two where the counts are few enough.
 //   k_count   one workgroup per token tile: one thread per token holds the
 //             token's ids in registers, checks them and counts them into the
 //             tile's expert histogram in LDS, written to tile_counts[tile][E].
