@@ -454,8 +454,8 @@ inline size_t solve_lds_bytes(const PlanShape &sh, bool bounded) {
 }
 
 // ---------------------------------------------------------------- water-fill solve
-// One 1024-thread workgroup; smem holds wf_lds() ints.
-__device__ __forceinline__ void solve_waterfill(const PlanShape &sh, const PlanPtrs &p,
+// One 1024-thread workgroup; smem holds wf_lds() ints. Returns the plan's status word.
+__device__ __forceinline__ int solve_waterfill(const PlanShape &sh, const PlanPtrs &p,
                                                 int32_t *smem, int Te, int st) {
     WfLds L;
     wf_lds(sh.E, sh.R, sh.pcap, smem, &L);
@@ -586,6 +586,7 @@ __device__ __forceinline__ void solve_waterfill(const PlanShape &sh, const PlanP
     }
     if (tid < R) p.seg_ptr[(int64_t)tid * sp + G + np] = h.keep + (s_dend[tid] - s_dbeg[tid]);
     solve_tail(sh, p, totNZ, &s_status, &s_maxT);
+    return s_status;
 }
 
 // T (from k_scan) and this thread's share of the tiles' status words.
@@ -627,6 +628,7 @@ struct PlaceArgs {
     const int *s_xl, *s_ov;
     const int *s_bin, *s_binD, *s_binK;  // deficit ranks in fill order: rank, D, keep
     int *s_first, *s_nd, *s_fill, *s_pe, *s_pr, *s_pstart, *s_pcnt, *s_pjj;
+    int *s_rkey, *s_rbin;  // place_pieces_sorted's records: key taken, place of the rank
 };
 
 // The placement, run by one wave: ranks in fill order, pieces by the rules
@@ -733,71 +735,183 @@ __device__ __forceinline__ int place_pieces(const PlaceArgs &a, bool packed) {
 // v_writelane_b32: reg with lane `lane` set to val (both wave-uniform).
 __device__ int amdgcn_writelane(int val, int lane, int reg) __asm("llvm.amdgcn.writelane.i32");
 
-// The same placement for at most 64 overflows whose rows fit 21 bits, with the
-// overflows kept sorted across the wave instead of searched: lane p holds the
-// overflow at position p of the order (rows left descending, then id ascending)
-// as the key ((rows - 1) << 10) | (kMaxE - 1 - id), and a wave-uniform mask has
-// a bit per lane whose overflow still has rows. Every rule then reads the first
-// (or last) set bit of a ballot:
-//   largest that fits whole  first live lane with key < room << 10
+// The same placement for at most 64 overflows whose rows fit 21 bits, deficits
+// of at most 2^21 rows and B <= 63, with the overflows kept sorted across the
+// wave instead of searched: lane p holds the overflow at position p of the order
+// (rows left descending, then id ascending) as the key
+// ((rows - 1) << 10) | (kMaxE - 1 - id), and a wave-uniform mask has a bit per
+// lane whose overflow still has rows. The rank's free room is kept as
+// T = room * 1024 - 1, so that "rows <= room" is "key <= T" and a full rank
+// (T = -1) matches no key. Every rule then reads the first (or last) set bit
+// of a ballot:
+//   largest that fits whole  first live lane with key <= T
 //   largest                  first live lane
-//   smallest that fills      the last live lane with key >= (room - 1) << 10
-//                            has the fewest rows; the first live lane with those
-//                            rows has the lowest id among them
+//   smallest that fills      the last live lane with key > T - 1024 has the
+//                            fewest rows; the first live lane with those rows
+//                            has the lowest id among them
 // A piece that cuts an overflow (always a rank's last) moves its key down past
 // the live keys that are now larger, the keys between moving up one lane (a
-// whole-wave DPP shift). One step is a chain of scalar work around
-// one ballot and one lane read; the pieces are recorded in three registers
-// (lane = piece mod 64: the key the piece was cut from, the rank's room before
-// it and the rank's place in fill order) and the ranks in three more (lane =
-// place mod 64), each written to LDS 64 at a time.
+// whole-wave DPP shift). A step is a short chain of scalar work around one
+// ballot and one lane read, and it records only the key it took and the rank's
+// place in fill order (lane = piece mod 64, written to LDS in windows of up to
+// 64); every other table follows from those two afterwards, in parallel
+// (expand_sorted_pieces), because all but a rank's last piece are whole.
 struct PieceRegs {
-    int key, room, bin;
+    int key, bin;
 };
 
-__device__ __forceinline__ void flush_pieces(const PlaceArgs &a, const PieceRegs &g, int base,
-                                             int count) {
-    const int lane = lane_id();
-    if (lane < count) {
-        const int q = base + lane;
-        const int v = (g.key >> 10) + 1, e = (kMaxE - 1) - (g.key & (kMaxE - 1));
-        a.s_pe[q] = e;
-        a.s_pr[q] = a.s_bin[g.bin];
-        a.s_pstart[q] = a.s_binK[g.bin] + (a.s_binD[g.bin] - g.room);
-        a.s_pcnt[q] = min(v, g.room);
-        a.s_pjj[q] = a.s_ov[e] - v;  // first overflow row of the piece
+// records of pieces from .. to - 1 (at most 64), piece q in lane q mod 64
+__device__ __forceinline__ void flush_window(const PlaceArgs &a, const PieceRegs &g, int from, int to) {
+    const int q = from + ((lane_id() - from) & 63);
+    if (q < to) {
+        a.s_rkey[q] = g.key;
+        a.s_rbin[q] = g.bin;
     }
 }
 
-// all 64 records, pieces base .. base + 63
-__device__ __forceinline__ void flush_pieces64(const PlaceArgs &a, const PieceRegs &g, int base) {
-    const int q = base + lane_id();
-    const int v = (g.key >> 10) + 1, e = (kMaxE - 1) - (g.key & (kMaxE - 1));
-    a.s_pe[q] = e;
-    a.s_pr[q] = a.s_bin[g.bin];
-    a.s_pstart[q] = a.s_binK[g.bin] + (a.s_binD[g.bin] - g.room);
-    a.s_pcnt[q] = min(v, g.room);
-    a.s_pjj[q] = a.s_ov[e] - v;
-}
+// Exit codes of run_ranks.
+constexpr int kRunDone = 0, kRunReload = 1, kRunFlush = 2, kRunFill = 3;
 
-struct BinRegs {
-    int r, D, first, nd, fill;  // lane j: rank and deficit of place base + j; its results
-};
-
-__device__ __forceinline__ void flush_bins(const PlaceArgs &a, const BinRegs &b, int count) {
-    if (lane_id() < count) {
-        a.s_first[b.r] = b.first;
-        a.s_nd[b.r] = b.nd;
-        a.s_fill[b.r] = b.fill;
-    }
+// The common steps of place_pieces_sorted in one block of scalar and vector
+// instructions, with no memory access: ranks from bi on, each taking whole fits
+// (its pieces 1 .. B-1) and, when none fits, a piece of the largest overflow,
+// which ends the rank. Written out by hand because the compiler's rendering of
+// the branches adds a scalar copy or select to every step, and a step is a
+// chain of dependent scalar and lane operations. On entry bi < nb, live != 0
+// and np <= npmax; D of rank bi is in lane bi mod 64 of Dl. Stops with
+//   kRunDone    every rank is done or no overflow is left
+//   kRunReload  bi reached a multiple of 64 (Dl holds the wrong ranks)
+//   kRunFlush   the next rank could overrun the 64 piece records (np > npmax)
+//   kRunFill    rank bi has taken B-1 whole fits and has room T left
+// The only backward branches follow an increment of used (< B-1) or of
+// bi (< nb), so the block always ends. Lane selects come from scalar
+// instructions only (M0 for lane writes, whose data is the one SGPR operand a
+// vector instruction may read); an SGPR read by a lane write is written by a
+// lane read at least two instructions earlier, and a DPP read of key follows
+// s_nop 1.
+__device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int lane, uint64_t &live,
+                                          int &bi, int &np, int nb, int fitp, int npmax, int &T,
+                                          int &code) {
+    uint64_t m, t;
+    int L, k, A, D, used;
+    int vn;
+    // every scalar operand as a wave-uniform value, as the SGPR constraints need
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    uint64_t lv = ((uint64_t)(uint32_t)uni((int)(live >> 32)) << 32) | (uint32_t)uni((int)live);
+    int b = uni(bi), n = uni(np);
+    const int nbu = uni(nb), fitu = uni(fitp), npmu = uni(npmax);
+    asm volatile(
+        ".Lrank%=:\n"
+        "  s_and_b32 %[L], %[bi], 63\n"
+        "  v_readlane_b32 %[D], %[dl], %[L]\n"
+        "  s_mov_b32 %[used], 0\n"
+        "  s_nop 1\n"
+        "  s_lshl_b32 %[T], %[D], 10\n"
+        "  s_add_i32 %[T], %[T], -1\n"
+        "  s_cmp_le_i32 %[fitp], 0\n"
+        "  s_cbranch_scc1 .Lfill%=\n"
+        ".Lfit%=:\n"
+        "  v_cmp_ge_i32 vcc, %[T], %[key]\n"
+        "  s_and_b64 %[m], vcc, %[live]\n"
+        "  s_cbranch_scc0 .Lnofit%=\n"
+        "  s_ff1_i32_b64 %[L], %[m]\n"
+        "  v_readlane_b32 %[k], %[key], %[L]\n"
+        "  s_mov_b32 m0, %[np]\n"
+        "  v_writelane_b32 %[gb], %[bi], m0\n"
+        "  s_bitset0_b64 %[live], %[L]\n"
+        "  v_writelane_b32 %[gk], %[k], m0\n"
+        "  s_andn2_b32 %[k], 0xfffffc00, %[k]\n"
+        "  s_add_i32 %[np], %[np], 1\n"
+        "  s_add_i32 %[T], %[T], %[k]\n"
+        "  s_add_i32 %[used], %[used], 1\n"
+        "  s_cmp_lt_i32 %[used], %[fitp]\n"
+        "  s_cbranch_scc1 .Lfit%=\n"
+        "  s_cmp_lt_i32 %[T], 0\n"
+        "  s_cbranch_scc1 .Lnext%=\n"
+        "  s_cmp_eq_u64 %[live], 0\n"
+        "  s_cbranch_scc1 .Ldone%=\n"
+        ".Lfill%=:\n"
+        "  s_mov_b32 %[code], 3\n"
+        "  s_branch .Lexit%=\n"
+        ".Lnofit%=:\n"
+        "  s_cmp_lt_i32 %[T], 0\n"
+        "  s_cbranch_scc1 .Lnext%=\n"
+        "  s_cmp_eq_u64 %[live], 0\n"
+        "  s_cbranch_scc1 .Ldone%=\n"
+        "  s_ff1_i32_b64 %[L], %[live]\n"
+        "  v_readlane_b32 %[k], %[key], %[L]\n"
+        "  s_mov_b32 m0, %[np]\n"
+        "  v_writelane_b32 %[gb], %[bi], m0\n"
+        "  s_add_i32 %[A], %[T], 1\n"
+        "  v_writelane_b32 %[gk], %[k], m0\n"
+        "  s_add_i32 %[np], %[np], 1\n"
+        "  s_sub_i32 %[k], %[k], %[A]\n"
+        "  v_cmp_lt_i32 vcc, %[k], %[key]\n"
+        "  s_and_b64 %[m], vcc, %[live]\n"
+        "  s_bitset0_b64 %[m], %[L]\n"
+        "  s_flbit_i32_b64 %[A], %[m]\n"
+        "  s_xor_b32 %[A], %[A], 63\n"
+        "  s_cmp_le_i32 %[A], %[L]\n"
+        "  s_cbranch_scc1 .Linplace%=\n"
+        "  s_nop 1\n"
+        "  v_mov_b32_dpp %[vn], %[key] wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+        "  v_cmp_le_i32 %[t], %[L], %[vl]\n"
+        "  v_cmp_gt_i32 vcc, %[A], %[vl]\n"
+        "  s_and_b64 vcc, vcc, %[t]\n"
+        "  s_sub_i32 %[D], 63, %[A]\n"
+        "  s_mov_b32 m0, %[A]\n"
+        "  v_cndmask_b32 %[key], %[key], %[vn], vcc\n"
+        "  v_writelane_b32 %[key], %[k], m0\n"
+        "  s_lshr_b64 %[t], -1, %[D]\n"
+        "  s_lshl_b64 %[m], -1, %[L]\n"
+        "  s_and_b64 %[t], %[t], %[m]\n"
+        "  s_lshr_b64 %[m], %[live], 1\n"
+        "  s_and_b64 %[m], %[m], %[t]\n"
+        "  s_andn2_b64 %[live], %[live], %[t]\n"
+        "  s_or_b64 %[live], %[live], %[m]\n"
+        "  s_bitset1_b64 %[live], %[A]\n"
+        "  s_branch .Lnext%=\n"
+        ".Linplace%=:\n"
+        "  s_mov_b32 m0, %[L]\n"
+        "  v_writelane_b32 %[key], %[k], m0\n"
+        ".Lnext%=:\n"
+        "  s_add_i32 %[bi], %[bi], 1\n"
+        "  s_cmp_ge_i32 %[bi], %[nb]\n"
+        "  s_cbranch_scc1 .Ldone%=\n"
+        "  s_and_b32 %[L], %[bi], 63\n"
+        "  s_cmp_eq_u32 %[L], 0\n"
+        "  s_cbranch_scc1 .Lreload%=\n"
+        "  s_cmp_gt_i32 %[np], %[npmax]\n"
+        "  s_cbranch_scc0 .Lrank%=\n"
+        "  s_mov_b32 %[code], 2\n"
+        "  s_branch .Lexit%=\n"
+        ".Lreload%=:\n"
+        "  s_mov_b32 %[code], 1\n"
+        "  s_branch .Lexit%=\n"
+        ".Ldone%=:\n"
+        "  s_mov_b32 %[code], 0\n"
+        ".Lexit%=:\n"
+        : [key] "+v"(key), [gk] "+v"(g.key), [gb] "+v"(g.bin), [live] "+s"(lv), [bi] "+s"(b),
+          [np] "+s"(n), [T] "=&s"(T), [code] "=&s"(code), [m] "=&s"(m), [t] "=&s"(t),
+          [L] "=&s"(L), [k] "=&s"(k), [A] "=&s"(A), [D] "=&s"(D), [used] "=&s"(used),
+          [vn] "=&v"(vn)
+        : [dl] "v"(Dl), [vl] "v"(lane), [nb] "s"(nbu), [fitp] "s"(fitu), [npmax] "s"(npmu)
+        : "vcc", "scc", "m0");
+    // the results are wave-uniform; say so, or they would be kept per lane
+    live = ((uint64_t)(uint32_t)uni((int)(lv >> 32)) << 32) | (uint32_t)uni((int)lv);
+    bi = uni(b);
+    np = uni(n);
+    T = uni(T);
+    code = uni(code);
 }
 
 __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
-    constexpr int kRowsCap = 1 << 21;  // rows of every overflow are below this
     const int lane = lane_id();
     const int n0 = __builtin_amdgcn_readfirstlane(a.n_items);
     const int nb = __builtin_amdgcn_readfirstlane(a.n_bins);
     const int fit_pieces = __builtin_amdgcn_readfirstlane(a.B - 1);
+    // records a rank adds before its fill steps: its whole fits and one more
+    const int need = max(fit_pieces, 0) + 1;
     int key = 0;
     if (lane < n0) {
         const int id = a.s_xl[lane];
@@ -812,92 +926,66 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
     }
     key = __builtin_amdgcn_ds_permute(pos << 2, key);
     uint64_t live = n0 >= 64 ? ~0ull : (1ull << n0) - 1;
+    constexpr uint64_t kTop = 1ull << 63;
 
     // No check against the piece tables' room: every piece but a rank's last
     // places an overflow whole, so pieces <= overflows + ranks - 1 < pcap.
-    PieceRegs g{0, 0, 0};
-    BinRegs b{0, 0, 0, 0, 0};
-    int np = 0, bi = 0;
+    PieceRegs g{0, 0};
+    int np = 0, fl = 0;  // pieces placed; pieces whose records are in LDS
+    int bi = 0;          // place of the rank in fill order
+    auto record = [&](int k) {
+        const int slot = np & 63;
+        g.key = amdgcn_writelane(k, slot, g.key);
+        g.bin = amdgcn_writelane(bi, slot, g.bin);
+        ++np;
+    };
+    // lane j: deficit of the rank at place (bi & ~63) + j
+    int Dl = lane < nb ? a.s_binD[lane] : 0;
     while (bi < nb && live != 0) {
-        const int bl = bi & 63;
-        if (bl == 0) {
+        // room for a rank's fit pieces and the step after them
+        if (np - fl > 64 - need) {
+            flush_window(a, g, fl, np);
+            fl = np;
+        }
+        // Ranks from bi on, while every step is a whole fit or a rank's last
+        // piece of the largest overflow; see run_ranks.
+        int T, code;
+        run_ranks(key, g, Dl, lane, live, bi, np, nb, fit_pieces, fl + 64 - need, T, code);
+        if (code == kRunDone) break;
+        if (code == kRunReload) {
             const int j = bi + lane;
-            b.r = j < nb ? a.s_bin[j] : 0;
-            b.D = j < nb ? a.s_binD[j] : 0;
+            Dl = j < nb ? a.s_binD[j] : 0;
+            continue;
         }
-        const int D = __builtin_amdgcn_readlane(b.D, bl);
-        int room = D, used = 0;
-        int cut = -1, ck = 0;  // lane and key of an overflow the rank's last piece cuts
-        const int first = np;
-        // A step writes its piece at lane np % 64 of the records and counts it
-        // only if the piece places its overflow whole; a piece that cuts is
-        // counted below, its record already written by the step that chose it.
-        // Each loop tests its exit at the bottom only; a step after the last
-        // live overflow is gone (bit 63 of an empty mask) counts nothing.
-        auto step = [&](int L, int k, bool whole) {
-            const int slot = np & 63;
-            g.key = amdgcn_writelane(k, slot, g.key);
-            g.room = amdgcn_writelane(room, slot, g.room);
-            g.bin = amdgcn_writelane(bi, slot, g.bin);
-            if (whole) {
-                ++np;
-                ++used;
-                room -= (k >> 10) + 1;
-                live &= ~(1ull << L);
-                if ((np & 63) == 0) flush_pieces64(a, g, np - 64);
+        if (code == kRunFlush) continue;
+        // kRunFill: rank bi has placed its fit pieces and has room left; the
+        // smallest overflow that fills the room (lowest id among those rows), or
+        // if none is that large the largest whole
+        int L, k;
+        bool cut;
+        for (;;) {
+            if (np - fl == 64) {
+                flush_window(a, g, fl, np);
+                fl = np;
             }
-        };
-        constexpr uint64_t kTop = 1ull << 63;
-        // pieces 1 .. B-1: the largest overflow that fits whole; if none fits
-        // (and rows are left), a piece of the largest
-        if (used < fit_pieces) {
-            bool fits;
-            int L, k;
-            do {
-                const int rc = min(room, kRowsCap);
-                const uint64_t m =
-                    __builtin_amdgcn_ballot_w64((unsigned)key < ((unsigned)rc << 10)) & live;
-                fits = m != 0;
-                L = __builtin_ctzll((fits ? m : live) | kTop);
-                k = __builtin_amdgcn_readlane(key, L);
-                step(L, k, fits);
-            } while (fits && used < fit_pieces);
-            if (!fits && room > 0 && live != 0) {
-                cut = L;
-                ck = k;
-            }
+            const uint64_t ge = __builtin_amdgcn_ballot_w64(key > T - kMaxE) & live;
+            const int h = 63 - __builtin_clzll(ge | 1);
+            const int kh = __builtin_amdgcn_readlane(key, h) & ~(kMaxE - 1);
+            const uint64_t eq =
+                __builtin_amdgcn_ballot_w64((unsigned)(key - kh) < (unsigned)kMaxE) & live;
+            L = __builtin_ctzll((ge != 0 ? eq : live) | kTop);
+            k = __builtin_amdgcn_readlane(key, L);
+            record(k);
+            cut = k > T;  // more rows than room: the piece fills the rank
+            if (cut) break;
+            T -= (k | (kMaxE - 1)) + 1;
+            live &= ~(1ull << L);
+            if (T < 0 || live == 0) break;
         }
-        // then the smallest overflow that fills the room (lowest id among those
-        // rows), or if none is that large the largest whole
-        if (cut < 0 && room > 0 && live != 0) {
-            bool whole;
-            int L, k;
-            do {
-                const int rc = min(room, kRowsCap);
-                const uint64_t ge = __builtin_amdgcn_ballot_w64(key >= ((rc - 1) << 10)) & live;
-                const int h = 63 - __builtin_clzll(ge | 1);
-                const int kh = __builtin_amdgcn_readlane(key, h) & ~(kMaxE - 1);
-                const uint64_t eq =
-                    __builtin_amdgcn_ballot_w64((unsigned)(key - kh) < (unsigned)kMaxE) & live;
-                L = __builtin_ctzll((ge != 0 ? eq : live) | kTop);
-                k = __builtin_amdgcn_readlane(key, L);
-                whole = live != 0 && (k >> 10) + 1 <= room;
-                step(L, k, whole);
-            } while (whole && room > 0);
-            if (!whole && live != 0) {
-                cut = L;
-                ck = k;
-            }
-        }
-        if (cut >= 0) {
+        if (cut) {
             // the overflow keeps rows: its key drops below the live keys of the
             // lanes up to A, which move up one lane with their bits
-            const int L = cut;
-            ++np;
-            ++used;
-            if ((np & 63) == 0) flush_pieces64(a, g, np - 64);
-            const int k2 = ck - (room << 10);
-            room = 0;
+            const int k2 = k - (T + 1);
             const uint64_t gt = __builtin_amdgcn_ballot_w64(key > k2) & live & ~(1ull << L);
             const int A = gt != 0 ? 63 - __builtin_clzll(gt) : -1;
             if (A > L) {
@@ -905,25 +993,51 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
                 const int next = __builtin_amdgcn_update_dpp(key, key, 0x130, 0xf, 0xf, false);
                 key = lane >= L && lane < A ? next : key;
                 key = amdgcn_writelane(k2, A, key);
-                const uint64_t span = ((2ull << A) - 1) & ~((1ull << L) - 1);  // bits L..A
+                const uint64_t span = (~0ull >> (63 - A)) & (~0ull << L);  // bits L..A
                 live = (live & ~span) | ((live >> 1) & span) | (1ull << A);
             } else {
                 key = amdgcn_writelane(k2, L, key);
             }
         }
-        b.first = amdgcn_writelane(first, bl, b.first);
-        b.nd = amdgcn_writelane(used, bl, b.nd);
-        b.fill = amdgcn_writelane(D - room, bl, b.fill);
         ++bi;
-        if ((bi & 63) == 0) flush_bins(a, b, 64);
+        if ((bi & 63) == 0 && bi < nb) {
+            const int j = bi + lane;
+            Dl = j < nb ? a.s_binD[j] : 0;
+        }
     }
-    if ((bi & 63) != 0) flush_bins(a, b, bi & 63);
-    if ((np & 63) != 0) flush_pieces(a, g, np & ~63, np & 63);
+    flush_window(a, g, fl, np);
     return np;
 }
 
-// One 1024-thread workgroup; smem holds bd_lds() ints.
-__device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtrs &p,
+// The tables of the pieces place_pieces_sorted recorded (key taken, place of the
+// rank in fill order), one thread per piece: a rank's pieces are consecutive,
+// all but its last take their overflow whole, and the last takes what is left
+// of the rank's deficit if that is less.
+__device__ __forceinline__ void expand_sorted_pieces(const PlaceArgs &a, int P) {
+    for (int q = threadIdx.x; q < P; q += kSolveThreads) {
+        const int k = a.s_rkey[q], bi = a.s_rbin[q];
+        int j = q, before = 0;  // the rank's first piece; rows of its pieces before q
+        while (j > 0 && a.s_rbin[j - 1] == bi) {
+            --j;
+            before += (a.s_rkey[j] >> 10) + 1;
+        }
+        const int v = (k >> 10) + 1, e = (kMaxE - 1) - (k & (kMaxE - 1));
+        const int r = a.s_bin[bi], cnt = min(v, a.s_binD[bi] - before);
+        a.s_pe[q] = e;
+        a.s_pr[q] = r;
+        a.s_pstart[q] = a.s_binK[bi] + before;
+        a.s_pcnt[q] = cnt;
+        a.s_pjj[q] = a.s_ov[e] - v;  // first overflow row of the piece
+        if (j == q) a.s_first[r] = q;
+        if (q + 1 == P || a.s_rbin[q + 1] != bi) {
+            a.s_nd[r] = q - j + 1;
+            a.s_fill[r] = before + cnt;
+        }
+    }
+}
+
+// One 1024-thread workgroup; smem holds bd_lds() ints. Returns the plan's status word.
+__device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs &p,
                                               int32_t *smem, int Te, int st) {
     BdLds L;
     bd_lds(sh.E, sh.R, sh.pcap, smem, &L);
@@ -999,13 +1113,14 @@ __device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtr
     __syncthreads();
 
     // 2. placement (wave 0), with as many register slots per lane as the overflows need
+    const PlaceArgs a{n_items, n_bins, B, sh.pcap, s_xl, s_ov, s_bin, s_binD, s_binK, s_first, s_nd,
+                      s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj, s_pkey, s_skey};
+    const int nslots = (n_items + 63) >> 6;
+    const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
+    const bool sorted = nslots <= 1 && packed && sh.SK <= (1 << 21) && B <= 63;
     if (w == 0) {
-        PlaceArgs a{n_items, n_bins, B, sh.pcap, s_xl, s_ov, s_bin, s_binD, s_binK,
-                    s_first, s_nd, s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj};
-        const int nslots = (n_items + 63) >> 6;
-        const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
         int np;
-        if (nslots <= 1 && packed) np = place_pieces_sorted(a);
+        if (sorted) np = place_pieces_sorted(a);
         else if (nslots <= 1) np = place_pieces<1, false>(a);
         else if (nslots <= 2) np = place_pieces<2>(a, packed);
         else if (nslots <= 4) np = place_pieces<4>(a, packed);
@@ -1020,6 +1135,10 @@ __device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtr
 
     // 3. tables: per rank (pieces in placement order), the list by (expert, rank)
     const int P = s_np;
+    if (sorted) {
+        expand_sorted_pieces(a, P);
+        __syncthreads();
+    }
     const int sp = G + sh.dcap + 1, se = G + sh.dcap;
     for (int q = tid; q < P; q += kSolveThreads) {
         const int r = s_pr[q], e = s_pe[q], b = q - s_first[r];
@@ -1074,6 +1193,7 @@ __device__ __forceinline__ void solve_bounded(const PlanShape &sh, const PlanPtr
     }
     if (tid < R && nd <= sh.dcap) p.seg_ptr[(int64_t)tid * sp + G + nd] = h.keep + s_fill[tid];
     solve_tail(sh, p, n_items, &s_status, &s_maxT);
+    return s_status;
 }
 
 __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
@@ -1407,15 +1527,15 @@ __device__ __forceinline__ void plan_tails(const PlanShape &sh, const PlanPtrs &
 }
 
 // The assign passes over one tile, once its ids are in idv and the plan tables
-// the placement needs are in regs (fetch_tables). smem holds assign_lds_bytes().
+// the placement needs are in regs (fetch_tables). by_tokens: K >= 4 and no
+// repeated ids in the plan's status (else the bit-slice ranks). smem holds
+// assign_lds_bytes().
 __device__ __forceinline__ void assign_tile(const PlanShape &sh, const PlanPtrs &p, const Tile &t,
                                             const int (&idv)[kChunks], const TableRegs &regs,
-                                            int32_t *smem) {
+                                            bool by_tokens, int32_t *smem) {
     uint32_t *s_pos = reinterpret_cast<uint32_t *>(smem);
     AsgTables tb;
     asg_tables(sh.E, sh.R, sh.pcap, tile_cap(sh), smem + pos_ints(sh), &tb);
-    // the solve has the final status: repeated ids take the bit-slice ranks
-    const bool by_tokens = sh.K >= 4 && !(p.status[0] & MOONEP_STATUS_REPEAT_ID);
     zero_pos(sh, s_pos);
     __syncthreads();
     int rank[kChunks];
@@ -1445,12 +1565,13 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
 void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
     const Tile t = tile_of(sh, blockIdx.x);
-    // loads first, all in flight: this wave's ids, then the tables, which are
-    // only needed once the ranks are taken
+    // loads first, all in flight: the status, this wave's ids, then the tables,
+    // which are only needed once the ranks are taken
+    const int status = p.status[0];
     int idv[kChunks];
     load_ids(sh, ids, t, idv);
     const TableRegs regs = fetch_tables(sh, p, t.tile, true);
-    assign_tile(sh, p, t, idv, regs, smem);
+    assign_tile(sh, p, t, idv, regs, sh.K >= 4 && !(status & MOONEP_STATUS_REPEAT_ID), smem);
 }
 
 // ---------------------------------------------------------------- k_plan_fused
@@ -1587,22 +1708,22 @@ __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__
     extern __shared__ int32_t smem[];
     const int tid = threadIdx.x;
     const Tile t = tile_of(sh, blockIdx.x);
-    // the tiles' status words and counts first, so that they share one round
-    // trip; this tile's ids are loaded after the solve, together with the tables
-    // (keeping them in registers across the solve would crowd it)
+    // the tiles' status words, this tile's ids and the counts first, so that
+    // they share one round trip and the ids are in by the time they are ranked
     int st = tid < sh.n_tiles ? p.tile_status[tid] : 0;
+    int idv[kChunks];
+    load_ids(sh, ids, t, idv);
     int Te, base;
     gather_counts<gather_unroll<BOUNDED>()>(sh, p, t.tile, Te, base, smem);
     for (int u = tid + kAssignThreads; u < sh.n_tiles; u += kAssignThreads) st |= p.tile_status[u];
     if (blockIdx.x == 0 && tid < sh.E) p.T[tid] = Te;
-    if constexpr (BOUNDED) solve_bounded(sh, p, smem, Te, st);
-    else solve_waterfill(sh, p, smem, Te, st);
+    int status;
+    if constexpr (BOUNDED) status = solve_bounded(sh, p, smem, Te, st);
+    else status = solve_waterfill(sh, p, smem, Te, st);
     __syncthreads();  // this workgroup's plan writes are visible to all its threads
-    int idv[kChunks];
-    load_ids(sh, ids, t, idv);
     TableRegs regs = fetch_tables(sh, p, t.tile, false);
     regs.tbase = base;
-    assign_tile(sh, p, t, idv, regs, smem);
+    assign_tile(sh, p, t, idv, regs, sh.K >= 4 && !(status & MOONEP_STATUS_REPEAT_ID), smem);
 }
 
 hipError_t allow_lds(const void *kernel, size_t lds) {
