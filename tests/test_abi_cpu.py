@@ -208,3 +208,20 @@ def test_binding_checks_tensors(td):
         td.moonep_plan(d, torch.zeros(512, dtype=torch.int32), torch.zeros(10, dtype=torch.uint8))
     with pytest.raises(TypeError):
         td.moonep_plan(d, [1, 2], None)
+
+
+def test_build_rejects_kernels_with_scratch():
+    """The build reads hipcc's resource-usage remarks and names every kernel
+    whose scratch size is nonzero (a launch of one sets up a private segment)."""
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "token_dispatch_amd"))
+    import build
+    remarks = "\n".join([
+        "plan.hip:1:1: remark: Function Name: k_a [-Rpass-analysis=kernel-resource-usage]",
+        "plan.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "plan.hip:9:1: remark: Function Name: k_b [-Rpass-analysis=kernel-resource-usage]",
+        "plan.hip:9:1: remark:     VGPRs: 123 [-Rpass-analysis=kernel-resource-usage]",
+        "plan.hip:9:1: remark:     ScratchSize [bytes/lane]: 36 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build._scratch_kernels(remarks) == ["k_b (36 bytes/lane)"]
+    assert build._scratch_kernels(remarks.replace(": 36 ", ": 0 ")) == []

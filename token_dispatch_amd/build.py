@@ -6,8 +6,13 @@ libmoonep_stream.so  the streaming kernels the benchmark measures ceilings with
 
 Every source is compiled for the device (gfx950 only) and linked next to this
 file. Packed-FP32 instruction selection is switched off for all device code.
+No kernel is meant to need scratch memory: a launch of one that does pays for
+setting up a private segment even when the frame is never touched, so the
+build reads the compiler's resource-usage remarks and fails on any kernel with
+a nonzero scratch size.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -32,9 +37,15 @@ def build(verbose: bool = False) -> str:
     procs = []
     objs = _compile(SOURCES, procs, verbose)
     stream_objs = _compile(STREAM_SOURCES, procs, verbose)
+    scratch = []
     for p, cmd in procs:
-        if p.wait() != 0:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
             raise RuntimeError("hipcc failed: " + " ".join(cmd))
+        scratch += _scratch_kernels(out)
+    if scratch:
+        raise RuntimeError("kernels that need scratch memory: " + ", ".join(scratch))
     _link(objs, LIB, verbose)
     _link(stream_objs, STREAM_LIB, verbose)
     return LIB
@@ -44,12 +55,27 @@ def _compile(sources, procs, verbose):
     objs = []
     for src in sources:
         obj = os.path.join(HERE, "_build", src.replace(".hip", ".o"))
-        cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage",
+                                 "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((subprocess.Popen(cmd), cmd))
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                       text=True), cmd))
         objs.append(obj)
     return objs
+
+
+def _scratch_kernels(remarks):
+    """Kernels whose resource-usage remark gives a nonzero scratch size."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append(f"{name} ({m.group(1)} bytes/lane)")
+    return out
 
 
 def _link(objs, lib, verbose):

@@ -132,6 +132,43 @@ __device__ __forceinline__ int lower_bound(const int *a, int n, int x) {
     return lo;
 }
 
+// Sum of v over each aligned group of GS consecutive lanes (GS = 1, 2, 4, 8 or
+// 16), in every lane of the group, by DPP moves inside rows; every lane of the
+// group must be active.
+template <int GS>
+__device__ __forceinline__ int group_sum(int v) {
+    if constexpr (GS >= 2) v += __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    if constexpr (GS >= 4) v += __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    if constexpr (GS >= 8) v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    if constexpr (GS >= 16) v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, false); // row_mirror
+    return v;
+}
+
+// Lanes per item when the workgroup counts, for each of n items, the keys that
+// order before it: 16 for 16 < n <= 64 items (four keys per lane), else one
+// thread per item.
+__device__ __forceinline__ int count_group(int n) { return n > 16 && n <= kSolveThreads / 16 ? 16 : 1; }
+
+// The keys among k[0 .. n) that order before x (before(k[j], x)), counted by
+// the gs lanes of the item (count_group); every lane of the group gets the total.
+template <class Key, class Before>
+__device__ __forceinline__ int group_count(const Key *k, int n, Key x, int gs, Before before) {
+    int c = 0;
+    if (gs == 16) {
+        const int sub = (int)threadIdx.x & 15;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = sub + 16 * u;
+            const bool b = before(k[min(j, n - 1)], x);
+            c += j < n && b ? 1 : 0;
+        }
+        return group_sum<16>(c);
+    }
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) c += before(k[j], x) ? 1 : 0;
+    return c;
+}
+
 // ---------------------------------------------------------------- k_count
 // KMAX: a power of two >= K; TPT tokens per thread cover the largest tile any K
 // in (KMAX/2, KMAX] gives. All of a thread's ids are loaded before any is used.
@@ -629,6 +666,7 @@ struct PlaceArgs {
     const int *s_bin, *s_binD, *s_binK;  // deficit ranks in fill order: rank, D, keep
     int *s_first, *s_nd, *s_fill, *s_pe, *s_pr, *s_pstart, *s_pcnt, *s_pjj;
     int *s_rkey, *s_rbin;  // place_pieces_sorted's records: key taken, place of the rank
+    const int *s_okey;     // place_pieces_sorted's overflow keys, already in order
 };
 
 // The placement, run by one wave: ranks in fill order, pieces by the rules
@@ -739,8 +777,8 @@ __device__ int amdgcn_writelane(int val, int lane, int reg) __asm("llvm.amdgcn.w
 // of at most 2^21 rows and B <= 63, with the overflows kept sorted across the
 // wave instead of searched: lane p holds the overflow at position p of the order
 // (rows left descending, then id ascending) as the key
-// ((rows - 1) << 10) | (kMaxE - 1 - id), and a wave-uniform mask has a bit per
-// lane whose overflow still has rows. The rank's free room is kept as
+// ((rows - 1) << 10) | (kMaxE - 1 - id), read from s_okey in that order, and a
+// wave-uniform mask has a bit per lane whose overflow still has rows. The rank's free room is kept as
 // T = room * 1024 - 1, so that "rows <= room" is "key <= T" and a full rank
 // (T = -1) matches no key. Every rule then reads the first (or last) set bit
 // of a ballot:
@@ -912,19 +950,7 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
     const int fit_pieces = __builtin_amdgcn_readfirstlane(a.B - 1);
     // records a rank adds before its fill steps: its whole fits and one more
     const int need = max(fit_pieces, 0) + 1;
-    int key = 0;
-    if (lane < n0) {
-        const int id = a.s_xl[lane];
-        key = ((a.s_ov[id] - 1) << 10) | (kMaxE - 1 - id);
-    }
-    // position of each key in descending order (the keys are distinct); empty
-    // lanes keep their own
-    int pos = lane;
-    if (lane < n0) {
-        pos = 0;
-        for (int j = 0; j < n0; ++j) pos += __builtin_amdgcn_readlane(key, j) > key ? 1 : 0;
-    }
-    key = __builtin_amdgcn_ds_permute(pos << 2, key);
+    int key = lane < n0 ? a.s_okey[lane] : 0;
     uint64_t live = n0 >= 64 ? ~0ull : (1ull << n0) - 1;
     constexpr uint64_t kTop = 1ull << 63;
 
@@ -1075,26 +1101,47 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
     int kv[3] = {kept, ov > 0 ? 1 : 0, tid < R && h.D > 0 ? 1 : 0}, kpre[3], ktot[3];
     block_excl_scan<3>(kv, kpre, ktot, s_w);
     const int n_items = ktot[1], n_bins = ktot[2];
+    // up to 64 overflows with rows below 2^21, deficits of at most 2^21 rows and
+    // B <= 63 take place_pieces_sorted
+    const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
+    const bool sorted = n_items <= 64 && packed && sh.SK <= (1 << 21) && B <= 63;
+    int *const s_ukey = s_T, *const s_okey = s_cum;  // T and its prefix are spent
     if (tid < E) {
         s_kc[tid] = kpre[0];
-        if (ov > 0) s_xl[kpre[1]] = tid;
+        if (ov > 0) {
+            s_xl[kpre[1]] = tid;
+            if (sorted) s_ukey[kpre[1]] = ((ov - 1) << 10) | (kMaxE - 1 - tid);
+        }
     }
     if (tid == 0) {
         s_kc[E] = ktot[0];
         s_np = 0;
         s_err = 0;
     }
-    if (tid < R && h.D > 0) {  // the rank's place in fill order
-        const uint64_t mine = s_bkey[tid];
-        int pos = 0;
-#pragma unroll 8
-        for (int r2 = 0; r2 < R; ++r2) pos += s_bkey[r2] > mine ? 1 : 0;
-        s_bin[pos] = tid;
-        s_binD[pos] = h.D;
-        s_binK[pos] = h.keep;
+    {  // each rank's place in fill order: the ranks whose key is larger, counted
+       // by a group of lanes per rank
+        const int gs = count_group(R), r = tid / gs;
+        if (r < R) {
+            const uint64_t mine = s_bkey[r];
+            const int pos = group_count(s_bkey, R, mine, gs,
+                                        [](uint64_t a, uint64_t b) { return a > b; });
+            if ((tid & (gs - 1)) == 0 && mine != 0) {
+                s_bin[pos] = r;
+                s_binD[pos] = s_D[r];
+                s_binK[pos] = s_keep[r];
+            }
+        }
     }
     int v2[2] = {h.O, h.D}, dpre[2], dtot[2];
     block_excl_scan<2>(v2, dpre, dtot, s_w);  // also orders the writes above
+    if (sorted) {  // the overflow keys in descending order (they are distinct)
+        const int gs = count_group(n_items), i = tid / gs;
+        if (i < n_items) {
+            const int x = s_ukey[i];
+            const int pos = group_count(s_ukey, n_items, x, gs, [](int a, int b) { return a > b; });
+            if ((tid & (gs - 1)) == 0) s_okey[pos] = x;
+        }
+    }
     if (tid < R) {
         p.Opre[tid] = dpre[0];
         p.Dpre[tid] = dpre[1];
@@ -1114,10 +1161,8 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
 
     // 2. placement (wave 0), with as many register slots per lane as the overflows need
     const PlaceArgs a{n_items, n_bins, B, sh.pcap, s_xl, s_ov, s_bin, s_binD, s_binK, s_first, s_nd,
-                      s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj, s_pkey, s_skey};
+                      s_fill, s_pe, s_pr, s_pstart, s_pcnt, s_pjj, s_pkey, s_skey, s_okey};
     const int nslots = (n_items + 63) >> 6;
-    const bool packed = s_maxT < (1 << 21);  // every overflow's rows fit a 21-bit key field
-    const bool sorted = nslots <= 1 && packed && sh.SK <= (1 << 21) && B <= 63;
     if (w == 0) {
         int np;
         if (sorted) np = place_pieces_sorted(a);
@@ -1169,18 +1214,22 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
         p.upre[R] = mtot[1];
         p.n_list[0] = P;
     }
-    for (int q = tid; q < P; q += kSolveThreads) {
-        const int key = s_pkey[q];
-        int pos = 0;
-#pragma unroll 8
-        for (int i = 0; i < P; ++i) pos += s_pkey[i] < key ? 1 : 0;
-        s_skey[pos] = key;
-        p.list_expert[pos] = s_pe[q];
-        p.list_rank[pos] = s_pr[q];
-        p.list_b[pos] = q - s_first[s_pr[q]];
-        p.piece_js[pos] = s_pjj[q];
-        p.pslot[pos] = s_pr[q] * sh.SK + s_pstart[q];
-        p.pcnt[pos] = s_pcnt[q];
+    {  // the list: each piece's place among the (expert, rank) keys, counted by a
+       // group of lanes per piece
+        const int gs = count_group(P);
+        for (int q = tid / gs; q < P; q += kSolveThreads / gs) {
+            const int key = s_pkey[q];
+            const int pos = group_count(s_pkey, P, key, gs, [](int a, int b) { return a < b; });
+            if ((tid & (gs - 1)) == 0) {
+                s_skey[pos] = key;
+                p.list_expert[pos] = s_pe[q];
+                p.list_rank[pos] = s_pr[q];
+                p.list_b[pos] = q - s_first[s_pr[q]];
+                p.piece_js[pos] = s_pjj[q];
+                p.pslot[pos] = s_pr[q] * sh.SK + s_pstart[q];
+                p.pcnt[pos] = s_pcnt[q];
+            }
+        }
     }
     __syncthreads();
     // CSR over experts: pieces of expert e are the keys in [e*R, (e+1)*R)
@@ -1708,11 +1757,13 @@ __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__
     extern __shared__ int32_t smem[];
     const int tid = threadIdx.x;
     const Tile t = tile_of(sh, blockIdx.x);
-    // the tiles' status words, this tile's ids and the counts first, so that
-    // they share one round trip and the ids are in by the time they are ranked
+    // the tiles' status words, (water-fill) this tile's ids and the counts
+    // first, so that they share one round trip and the ids are in by the time
+    // they are ranked; the bounded solve needs the registers the ids would hold
+    // across it, so there they are loaded after the solve
     int st = tid < sh.n_tiles ? p.tile_status[tid] : 0;
     int idv[kChunks];
-    load_ids(sh, ids, t, idv);
+    if constexpr (!BOUNDED) load_ids(sh, ids, t, idv);
     int Te, base;
     gather_counts<gather_unroll<BOUNDED>()>(sh, p, t.tile, Te, base, smem);
     for (int u = tid + kAssignThreads; u < sh.n_tiles; u += kAssignThreads) st |= p.tile_status[u];
@@ -1721,6 +1772,7 @@ __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__
     if constexpr (BOUNDED) status = solve_bounded(sh, p, smem, Te, st);
     else status = solve_waterfill(sh, p, smem, Te, st);
     __syncthreads();  // this workgroup's plan writes are visible to all its threads
+    if constexpr (BOUNDED) load_ids(sh, ids, t, idv);
     TableRegs regs = fetch_tables(sh, p, t.tile, false);
     regs.tbase = base;
     assign_tile(sh, p, t, idv, regs, sh.K >= 4 && !(status & MOONEP_STATUS_REPEAT_ID), smem);
