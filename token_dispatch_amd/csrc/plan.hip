@@ -37,6 +37,8 @@
 // earlier entries with id e. That count is split as (earlier tiles) + (earlier
 // waves of this tile) + (earlier entries of this wave), each an integer count
 // taken in entry order.
+#include <atomic>
+
 #include "internal.h"
 
 namespace moonep {
@@ -808,27 +810,29 @@ __device__ __forceinline__ void flush_window(const PlaceArgs &a, const PieceRegs
 }
 
 // Exit codes of run_ranks.
-constexpr int kRunDone = 0, kRunReload = 1, kRunFlush = 2, kRunFill = 3;
+constexpr int kRunDone = 0, kRunStop = 1, kRunFlush = 2, kRunFill = 3;
 
 // The common steps of place_pieces_sorted in one block of scalar and vector
 // instructions, with no memory access: ranks from bi on, each taking whole fits
 // (its pieces 1 .. B-1) and, when none fits, a piece of the largest overflow,
 // which ends the rank. Written out by hand because the compiler's rendering of
 // the branches adds a scalar copy or select to every step, and a step is a
-// chain of dependent scalar and lane operations. On entry bi < nb, live != 0
-// and np <= npmax; D of rank bi is in lane bi mod 64 of Dl. Stops with
-//   kRunDone    every rank is done or no overflow is left
-//   kRunReload  bi reached a multiple of 64 (Dl holds the wrong ranks)
+// chain of dependent scalar and lane operations. On entry B >= 2, bi < bstop,
+// live != 0 and np <= npmax; D of rank bi is in lane bi mod 64 of Dl, and
+// bstop is the next multiple of 64 after bi or the number of ranks, if less.
+// Stops with
+//   kRunDone    no overflow is left
+//   kRunStop    bi reached bstop (Dl holds the wrong ranks, or every rank is done)
 //   kRunFlush   the next rank could overrun the 64 piece records (np > npmax)
 //   kRunFill    rank bi has taken B-1 whole fits and has room T left
 // The only backward branches follow an increment of used (< B-1) or of
-// bi (< nb), so the block always ends. Lane selects come from scalar
+// bi (< bstop), so the block always ends. Lane selects come from scalar
 // instructions only (M0 for lane writes, whose data is the one SGPR operand a
 // vector instruction may read); an SGPR read by a lane write is written by a
 // lane read at least two instructions earlier, and a DPP read of key follows
 // s_nop 1.
 __device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int lane, uint64_t &live,
-                                          int &bi, int &np, int nb, int fitp, int npmax, int &T,
+                                          int &bi, int &np, int bstop, int fitp, int npmax, int &T,
                                           int &code) {
     uint64_t m, t;
     int L, k, A, D, used;
@@ -837,17 +841,14 @@ __device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int la
     auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
     uint64_t lv = ((uint64_t)(uint32_t)uni((int)(live >> 32)) << 32) | (uint32_t)uni((int)live);
     int b = uni(bi), n = uni(np);
-    const int nbu = uni(nb), fitu = uni(fitp), npmu = uni(npmax);
+    const int nbu = uni(bstop), fitu = uni(fitp), npmu = uni(npmax);
     asm volatile(
         ".Lrank%=:\n"
         "  s_and_b32 %[L], %[bi], 63\n"
         "  v_readlane_b32 %[D], %[dl], %[L]\n"
         "  s_mov_b32 %[used], 0\n"
-        "  s_nop 1\n"
         "  s_lshl_b32 %[T], %[D], 10\n"
         "  s_add_i32 %[T], %[T], -1\n"
-        "  s_cmp_le_i32 %[fitp], 0\n"
-        "  s_cbranch_scc1 .Lfill%=\n"
         ".Lfit%=:\n"
         "  v_cmp_ge_i32 vcc, %[T], %[key]\n"
         "  s_and_b64 %[m], vcc, %[live]\n"
@@ -868,7 +869,6 @@ __device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int la
         "  s_cbranch_scc1 .Lnext%=\n"
         "  s_cmp_eq_u64 %[live], 0\n"
         "  s_cbranch_scc1 .Ldone%=\n"
-        ".Lfill%=:\n"
         "  s_mov_b32 %[code], 3\n"
         "  s_branch .Lexit%=\n"
         ".Lnofit%=:\n"
@@ -914,16 +914,13 @@ __device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int la
         "  v_writelane_b32 %[key], %[k], m0\n"
         ".Lnext%=:\n"
         "  s_add_i32 %[bi], %[bi], 1\n"
-        "  s_cmp_ge_i32 %[bi], %[nb]\n"
-        "  s_cbranch_scc1 .Ldone%=\n"
-        "  s_and_b32 %[L], %[bi], 63\n"
-        "  s_cmp_eq_u32 %[L], 0\n"
-        "  s_cbranch_scc1 .Lreload%=\n"
+        "  s_cmp_eq_u32 %[bi], %[bstop]\n"
+        "  s_cbranch_scc1 .Lstop%=\n"
         "  s_cmp_gt_i32 %[np], %[npmax]\n"
         "  s_cbranch_scc0 .Lrank%=\n"
         "  s_mov_b32 %[code], 2\n"
         "  s_branch .Lexit%=\n"
-        ".Lreload%=:\n"
+        ".Lstop%=:\n"
         "  s_mov_b32 %[code], 1\n"
         "  s_branch .Lexit%=\n"
         ".Ldone%=:\n"
@@ -933,7 +930,7 @@ __device__ __forceinline__ void run_ranks(int &key, PieceRegs &g, int Dl, int la
           [np] "+s"(n), [T] "=&s"(T), [code] "=&s"(code), [m] "=&s"(m), [t] "=&s"(t),
           [L] "=&s"(L), [k] "=&s"(k), [A] "=&s"(A), [D] "=&s"(D), [used] "=&s"(used),
           [vn] "=&v"(vn)
-        : [dl] "v"(Dl), [vl] "v"(lane), [nb] "s"(nbu), [fitp] "s"(fitu), [npmax] "s"(npmu)
+        : [dl] "v"(Dl), [vl] "v"(lane), [bstop] "s"(nbu), [fitp] "s"(fitu), [npmax] "s"(npmu)
         : "vcc", "scc", "m0");
     // the results are wave-uniform; say so, or they would be kept per lane
     live = ((uint64_t)(uint32_t)uni((int)(lv >> 32)) << 32) | (uint32_t)uni((int)lv);
@@ -974,13 +971,21 @@ __device__ __forceinline__ int place_pieces_sorted(const PlaceArgs &a) {
             fl = np;
         }
         // Ranks from bi on, while every step is a whole fit or a rank's last
-        // piece of the largest overflow; see run_ranks.
-        int T, code;
-        run_ranks(key, g, Dl, lane, live, bi, np, nb, fit_pieces, fl + 64 - need, T, code);
+        // piece of the largest overflow; see run_ranks. With B <= 1 a rank has
+        // no fit pieces, and every rank takes the fill steps below.
+        int T, code = kRunFill;
+        if (fit_pieces > 0) {
+            const int bstop = min(nb, (bi & ~63) + 64);
+            run_ranks(key, g, Dl, lane, live, bi, np, bstop, fit_pieces, fl + 64 - need, T, code);
+        } else {
+            T = (int)(((unsigned)__builtin_amdgcn_readlane(Dl, bi & 63) << 10) - 1u);
+        }
         if (code == kRunDone) break;
-        if (code == kRunReload) {
-            const int j = bi + lane;
-            Dl = j < nb ? a.s_binD[j] : 0;
+        if (code == kRunStop) {
+            if (bi < nb) {
+                const int j = bi + lane;
+                Dl = j < nb ? a.s_binD[j] : 0;
+            }
             continue;
         }
         if (code == kRunFlush) continue;
@@ -1778,9 +1783,27 @@ __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__
     assign_tile(sh, p, t, idv, regs, sh.K >= 4 && !(status & MOONEP_STATUS_REPEAT_ID), smem);
 }
 
-hipError_t allow_lds(const void *kernel, size_t lds) {
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS one workgroup may hold on gfx950
+
+// Launches with more dynamic LDS than the default 64 KiB need the kernel's limit
+// raised. It is raised once per kernel and device, to the whole kMaxLdsBytes,
+// so that a plan call makes no attribute call after the first (the host's time
+// between the plan's launches is time the device can sit idle).
+enum LdsKernel { kLdsFusedBounded, kLdsFused, kLdsSolveBounded, kLdsSolve, kLdsAssign, kLdsKernels };
+constexpr int kLdsDevices = 64;
+std::atomic<uint8_t> g_lds_raised[kLdsDevices][kLdsKernels];
+
+hipError_t allow_lds(const void *kernel, LdsKernel which, size_t lds) {
     if (lds <= 65536) return hipSuccess;  // within the default dynamic LDS limit of a launch
-    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > kMaxLdsBytes) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kLdsDevices;
+    if (cached && g_lds_raised[dev][which].load(std::memory_order_acquire)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+    if (e == hipSuccess && cached) g_lds_raised[dev][which].store(1, std::memory_order_release);
+    return e;
 }
 
 }  // namespace
@@ -1812,7 +1835,7 @@ hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &
         const size_t part = gather_part_bytes(sh, bounded);
         lds = lds > part ? lds : part;
         const void *k = bounded ? (const void *)k_plan_fused<true> : (const void *)k_plan_fused<false>;
-        hipError_t e = allow_lds(k, lds);
+        hipError_t e = allow_lds(k, bounded ? kLdsFusedBounded : kLdsFused, lds);
         if (e != hipSuccess) return e;
         if (bounded)
             hipLaunchKernelGGL(k_plan_fused<true>, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
@@ -1823,12 +1846,13 @@ hipError_t launch_plan(const PlanShape &sh, const int32_t *ids, const PlanPtrs &
     hipLaunchKernelGGL(k_scan, dim3((sh.E + 63) / 64), dim3(kScanThreads), 0, st, sh,
                        p.tile_counts, p.T);
     const size_t slds = solve_lds_bytes(sh, bounded);
-    hipError_t e = allow_lds(bounded ? (const void *)k_solve_bounded : (const void *)k_solve, slds);
+    hipError_t e = allow_lds(bounded ? (const void *)k_solve_bounded : (const void *)k_solve,
+                             bounded ? kLdsSolveBounded : kLdsSolve, slds);
     if (e != hipSuccess) return e;
     if (bounded) hipLaunchKernelGGL(k_solve_bounded, dim3(1), dim3(kSolveThreads), slds, st, sh, p);
     else hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), slds, st, sh, p);
     const size_t lds = assign_lds_bytes(sh);
-    e = allow_lds((const void *)k_assign, lds);
+    e = allow_lds((const void *)k_assign, kLdsAssign, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_assign, tiles, dim3(kAssignThreads), lds, st, ids, sh, p);
     return hipGetLastError();
