@@ -450,7 +450,7 @@ __host__ __device__ inline int wf_lds(int E, int R, int pcap, int32_t *base, WfL
 }
 
 struct BdLds {
-    uint64_t *bkey;
+    uint64_t *bkey, *ekey;
     int32_t *T, *cum, *kc, *ov, *xl, *bin, *binD, *binK, *keep, *O, *D, *nd, *first, *fill;
     int32_t *pe, *pr, *pstart, *pcnt, *pjj, *pkey, *skey, *w, *scal;
 };
@@ -459,6 +459,7 @@ __host__ __device__ inline int bd_lds(int E, int R, int pcap, int32_t *base, BdL
     LdsCarve c{base, 0};
     BdLds l;
     l.bkey = reinterpret_cast<uint64_t *>(c.take(2 * R));  // first: 8-byte aligned
+    l.ekey = reinterpret_cast<uint64_t *>(c.take(2 * E));  // expert order within a rank
     l.T = c.take(E);
     l.cum = c.take(E + 1);
     l.kc = c.take(E + 1);      // exclusive prefix of kept rows
@@ -1083,19 +1084,23 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
     const int E = sh.E, R = sh.R, G = sh.G, B = sh.B;
+    // each expert's place in its rank's overflow order (T descending, then id)
+    // as one key, T in the high word; solve_head's first barrier publishes them
+    uint64_t *const s_ekey = L.ekey;
+    if (tid < E) s_ekey[tid] = ((uint64_t)(uint32_t)Te << 32) | (uint32_t)~tid;
     const Head h = solve_head(sh, p, Te, st, s_T, s_cum, s_keep, s_O, s_D, s_w, &s_status, &s_maxT);
 
     // 1. overflow of each overloaded rank, from its largest experts
     int ov = 0;
     if (tid < E) {
         const int r = tid / G;
+        const uint64_t mine = s_ekey[tid];
         int before = 0;  // rows of the rank's experts that come before this one
         // branch-free and unrolled, so that the LDS reads go out together
 #pragma unroll 8
         for (int e2 = r * G; e2 < (r + 1) * G; ++e2) {
-            const int t2 = s_T[e2];
-            const bool ahead = (t2 > h.Te) | ((t2 == h.Te) & (e2 < tid));
-            before += ahead ? t2 : 0;
+            const uint64_t k2 = s_ekey[e2];
+            before += k2 > mine ? (int)(k2 >> 32) : 0;
         }
         ov = min(max(s_O[r] - before, 0), h.Te);
         s_ov[tid] = ov;
