@@ -375,7 +375,8 @@ def _deficits(total, hi, seed):
 # Routings built from per-expert counts for the edges of the bounded placement:
 # exactly 64 overflows (every lane of the sorted wave live) and 65 (the register-
 # slot search), ties in rows, B = 1 (no fit-whole pieces), overflows cut over many
-# deficit ranks, and deficits of more than 2^21 rows with every overflow below it.
+# deficit ranks, deficits of more than 2^21 rows with every overflow below it,
+# more than 64 deficit ranks, and B = 2, 63 and 64.
 def _edge_cases():
     def rows(over):
         return sum(sum(x) for x in over)
@@ -393,6 +394,16 @@ def _edge_cases():
     SK = (1 << 21) + (1 << 20)
     q = SK // 4
     out.append(("room_past_2p21", 2, 4, 1, SK, 2, [[q - 1000, q, q, q - 1000]], [SK - 2000]))
+    # more than 64 deficit ranks with at most 64 overflows: the sorted placement
+    # reloads the deficits every 64 ranks and flushes its piece records many times
+    few = [[10 + 3 * (i % 5)] for i in range(24)]
+    out.append(("ranks_past_64_b4", 256, 1, 2, 64, 4, few, _deficits(rows(few), 5, 6)))
+    out.append(("ranks_past_64_b2", 256, 1, 2, 64, 2, few, _deficits(rows(few), 5, 7)))
+    # B = 63, the largest the sorted placement takes (a flush before almost every
+    # rank), and B = 64, which takes the register-slot search
+    many = [[1 + (i % 5)] for i in range(60)]
+    out.append(("b63", 256, 1, 4, 16, 63, many, _deficits(rows(many), 40, 8)))
+    out.append(("b64", 256, 1, 4, 16, 64, many, _deficits(rows(many), 40, 8)))
     return out
 
 
