@@ -420,6 +420,38 @@ def test_bounded_placement_edges(td, case, bounded):
     assert int((g["O"] > 0).sum()) == n_over
 
 
+def _random_shapes(n, seed):
+    """Seeded random shapes of up to about 60 000 entries: 1 to 512 ranks of 1 to 8
+    experts, K from 1 to 16, B from 0 to 200, router skew from none to strong, bf16
+    and fp32 rows of one 16-byte chunk. They reach both launch forms, both
+    placement paths of the bounded plan (up to 64 overflowing experts and more),
+    ranks that take several duplicates, and B of 0, 1 and past every rank's need."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 5, 8, 16, 24, 32, 64, 96, 128, 256, 512]))
+        G = int(rng.integers(1, max(2, min(8, 1024 // R) + 1)))
+        K = int(rng.integers(1, min(R * G, 16) + 1))
+        S = int(rng.integers(1, max(1, 60000 // (R * K)) + 1))
+        B = int(rng.choice([0, 1, 2, 3, 4, 6, 8, 16, 31, 63, 64, 200]))
+        skew = float(rng.choice([0.0, 0.5, 1.0, 2.0, 3.0, 5.0]))
+        dt = W.BF16 if rng.random() < 0.5 else W.F32
+        out.append(_wl(f"rand{i}", R, R * G, K, S, B, 8 if dt == W.BF16 else 4, dt, skew))
+    return out
+
+
+RANDOM = _random_shapes(64, 11)
+
+
+@PLANS
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_shapes(td, wl, bounded):
+    """Every plan array, dispatch, combine, replicate and reduce against the oracle,
+    and the plan invariants, on seeded random shapes and routings."""
+    ids, w = W.make_routing(wl, 100 + int(wl.name[4:]))
+    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 6, bounded)
+
+
 def test_identity_expert_mean_returns_hidden(td):
     """y = recv and w = 1/K with K a power of two: combine gives back hidden bit for bit."""
     wl = _wl("identity", 8, 64, 8, 900, 8, 512, W.BF16, 2.0)
