@@ -35,6 +35,18 @@ def test_exports_every_declared_function(td):
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_the_header(td):
+    """Every MOONEP_ enum value of the header has the same value in the binding
+    (MOONEP_X as td.X), and so has the static scratch size."""
+    text = open(HEADER).read()
+    found = re.findall(r"MOONEP_([A-Z_0-9]+) *= *(-?[0-9]+)", text)
+    assert len(found) == 15
+    for name, value in found:
+        assert getattr(td, name) == int(value), name
+    m = re.search(r"#define MOONEP_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert td.STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
 def test_stream_library_exports_its_header():
     """libmoonep_stream.so (the ceiling kernels) exports what moonep_stream.h declares,
     and every header under include/ belongs to one of the two libraries."""

@@ -20,7 +20,7 @@ import oracle
 import workloads as W
 from tests.gpu_common import (HostStage, bf16_bits, local_dst, read_plan, run_plan, say,
                               token_batches)
-from tests.test_gpu_parity import SMALL, _dims, _host_rows, _wl
+from tests.test_gpu_parity import RANDOM_ROWS, SMALL, _dims, _host_rows, _wl
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,14 @@ def _small_case(td, wl, ids, w, seed):
         gout_h = _host_rows(gout).reshape(wl.n_tok, wl.H)
         grad_y = torch.full((wl.R, wl.SK, wl.H), 3.0, dtype=y.dtype, device=DEV)
         grad_w = torch.full((wl.R, wl.S, wl.K), 5.0, dtype=torch.float32, device=DEV)
+        if wl.H * (2 if g_dt == W.BF16 else 4) % 16:
+            # grad_out rows must be whole 16-byte chunks: rejected, nothing written
+            with pytest.raises(td.MoonEPError) as err:
+                td.moonep_combine_backward(dims, plan_buf, gout_d, w_d, y_d, grad_y, grad_w)
+            assert err.value.rc == td.ERR_DIMS
+            torch.cuda.synchronize()
+            assert bool((grad_w == 5.0).all()) and bool((grad_y == 3.0).all())
+            continue
         td.moonep_combine_backward(dims, plan_buf, gout_d, w_d, y_d, grad_y, grad_w)
         torch.cuda.synchronize()
         want_y = oracle.combine_backward_y(p["dst"], wl.K, gout_h, w, g_dt, wl.dtype)
@@ -113,6 +121,13 @@ def _small_case(td, wl, ids, w, seed):
 def test_backward_small_shapes_elementwise(td, wl):
     ids, w = W.make_routing(wl, seed=8)
     _small_case(td, wl, ids.reshape(-1), w.reshape(-1), 8)
+
+
+@pytest.mark.parametrize("wl", RANDOM_ROWS, ids=[w.name for w in RANDOM_ROWS])
+def test_backward_random_row_widths(td, wl):
+    """The backward moves at seeded random row widths and K."""
+    ids, w = W.make_routing(wl, 300 + int(wl.name[4:]))
+    _small_case(td, wl, ids.reshape(-1), w.reshape(-1), 9)
 
 
 def test_backward_with_dropped_entries(td):

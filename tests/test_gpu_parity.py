@@ -452,6 +452,40 @@ def test_random_shapes(td, wl, bounded):
     _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 6, bounded)
 
 
+def _random_rows(n, seed):
+    """Seeded random row widths for the moves: any multiple of 16 bytes from 16 B
+    to 40 KiB in bf16 and fp32 (every chunks-per-lane width, ragged lanes, rows of
+    several segments), K from 1 to 64, about 2 to 60 MiB of rows, and weight
+    blocks of random 16-byte multiples."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = W.BF16 if rng.random() < 0.5 else W.F32
+        chunks = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 2561))]))
+        H = chunks * (8 if dt == W.BF16 else 4)
+        R = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        G = int(rng.integers(1, 9))
+        K = int(rng.integers(1, min(R * G, 64) + 1))
+        S = max(1, int(rng.integers(1 << 21, 60 << 20)) // (R * K * chunks * 16))
+        B = int(rng.choice([0, 1, 2, 4, 8]))
+        blk = (int(rng.integers(1, 9)), 8 * int(rng.integers(1, 33)))
+        out.append(_wl(f"rows{i}", R, R * G, K, S, B, H, dt, float(rng.choice([0.0, 1.0, 3.0])),
+                       block=blk))
+    return out
+
+
+RANDOM_ROWS = _random_rows(24, 12)
+
+
+@pytest.mark.parametrize("wl", RANDOM_ROWS, ids=[w.name for w in RANDOM_ROWS])
+def test_random_row_widths(td, wl):
+    """The moves at seeded random row widths, K and weight blocks, element by
+    element against the oracle (odd cases take the bounded plan)."""
+    i = int(wl.name[4:])
+    ids, w = W.make_routing(wl, 200 + i)
+    _full_case(td, wl, ids.reshape(-1), w.reshape(-1), 7, bool(i & 1))
+
+
 def test_identity_expert_mean_returns_hidden(td):
     """y = recv and w = 1/K with K a power of two: combine gives back hidden bit for bit."""
     wl = _wl("identity", 8, 64, 8, 900, 8, 512, W.BF16, 2.0)

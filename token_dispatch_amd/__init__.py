@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 F32 = 0
 BF16 = 1
 STATIC_SCRATCH_BYTES = 8 << 20  # MOONEP_STATIC_SCRATCH_BYTES
+OK, ERR_DIMS, ERR_PTR, ERR_HIP, ERR_SIZE = 0, -1, -2, -3, -4
 STATUS_BAD_ID, STATUS_REPEAT_ID, STATUS_OVER_B = 1, 2, 4
 OP_DISPATCH, OP_COMBINE = 1, 2
 PLAN_BOUNDED, PLAN_FOUR_LAUNCH, PLAN_TWO_LAUNCH = 1, 2, 4
