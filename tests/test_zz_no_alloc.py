@@ -109,3 +109,26 @@ def test_noscratch_plan_equals_plan_calls_in_a_row(td, bounded):
         say(f"  equal (dups per rank max {int(g_small['n_dup'].max())}, "
             f"status {int(g_small['status'][0])})")
         del full, span, small, guard
+
+
+def test_noscratch_random_shapes_in_a_row(td):
+    """Seeded random shapes one after another through the same static array, both
+    plans alternating: each plan equals the regular call's."""
+    from tests.test_gpu_parity import RANDOM
+    for i, wl in enumerate(RANDOM[:24]):
+        bounded = bool(i & 1)
+        dims = _dims(td, wl)
+        lay = td.moonep_plan_layout(dims)
+        assert lay.bytes - lay.persist_bytes <= td.STATIC_SCRATCH_BYTES
+        say(f"noscratch {wl.name} bounded={bounded}: {dims}")
+        ids, _ = W.make_routing(wl, 100 + i)
+        ids_d = torch.from_numpy(ids).to(DEV)
+        full = torch.full((lay.bytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        small = torch.full((lay.persist_bytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        (td.moonep_plan_bounded if bounded else td.moonep_plan)(dims, ids_d, full)
+        td.moonep_plan_noscratch(dims, ids_d, small, bounded)
+        torch.cuda.synchronize()
+        assert_plan_equal(read_plan(td, dims, small), read_plan(td, dims, full))
+        m0, n0, x0 = _persist_ws(td, dims, full)
+        m1, n1, x1 = _persist_ws(td, dims, small)
+        assert np.array_equal(m0, m1) and n0 == n1 and np.array_equal(x0, x1)
