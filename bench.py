@@ -70,13 +70,16 @@ OP_KERNELS = {"plan": ("k_count", "k_scan", "k_solve", "k_solve_bounded", "k_ass
 COPY_CAL_BYTES = 1 << 30
 
 
-def traffic_for(op: str):
+def traffic_for(op: str, workload: str, plan: str):
     """HBM bytes per call of `op` from the committed counter summary, if it was
-    taken on the current sources of that call's kernels; else None."""
+    taken on this workload and plan and on the current sources of that call's
+    kernels; else None."""
     if not os.path.exists(TRAFFIC_PATH):
         return None
     with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload or rec.get("plan") != plan:
+        return None
     k = rec.get("ops", {}).get(op)
     if k is None or k.get("source_hash") != kernel_source_hash(OP_SOURCES[op]):
         return None
@@ -97,12 +100,14 @@ def _pmc_rows(csv_path: str, counter: str):
     return [(k, v[0], v[1]) for k, v in sorted(out.items())]
 
 
-def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, command: str) -> dict:
+def traffic_from_pmc(fetch_csv: str, write_csv: str, steps: int, warmup: int, command: str,
+                     workload: str, plan: str) -> dict:
     """HBM bytes per C-ABI call from two rocprofv3 --pmc runs of this benchmark
-    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
-    counter reads for the plain device copy of COPY_CAL_BYTES that
-    --copy-calibration enqueues after the timed steps."""
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) on `workload` and `plan`, each
+    scaled by what the same counter reads for the plain device copy of
+    COPY_CAL_BYTES that --copy-calibration enqueues after the timed steps."""
     rec = {"kernel_source_hash": kernel_source_hash(), "command": command,
+           "workload": workload, "plan": plan,
            "copy_calibration_bytes": COPY_CAL_BYTES, "ops": {}}
     calls = steps + warmup
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -466,7 +471,7 @@ def main():
 
     if args.traffic_from:
         rec = traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.steps,
-                               args.warmup, args.traffic_command)
+                               args.warmup, args.traffic_command, args.workload, args.plan)
         with open(TRAFFIC_PATH, "w") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
             f.write("\n")
@@ -616,7 +621,7 @@ def main():
 
     dom = max(("dispatch", "combine"), key=lambda o: op_ms[o])
     src_hash = kernel_source_hash()
-    traffic = traffic_for(dom)
+    traffic = traffic_for(dom, args.workload, args.plan)
     # one C-ABI call is n back-to-back launches of the kernel over token chunks;
     # the events bracket the call, so a launch takes the call's time over n on
     # average and moves the call's bytes over n on average

@@ -57,7 +57,8 @@ def test_traffic_from_pmc_scales_by_the_calibration_copy(tmp_path):
     fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
     _write_csv(fp, "FETCH_SIZE", rows_f)
     _write_csv(wp, "WRITE_SIZE", rows_w)
-    rec = bench.traffic_from_pmc(str(fp), str(wp), steps, warmup, "cmd")
+    rec = bench.traffic_from_pmc(str(fp), str(wp), steps, warmup, "cmd", "k3", "waterfill")
+    assert rec["workload"] == "k3" and rec["plan"] == "waterfill"
     assert rec["fetch_size_scale"] == pytest.approx(2.0)
     assert rec["write_size_scale"] == pytest.approx(1.0)
     d = rec["ops"]["dispatch"]
@@ -70,14 +71,25 @@ def test_traffic_from_pmc_scales_by_the_calibration_copy(tmp_path):
     assert d["source_hash"] == bench.kernel_source_hash(bench.OP_SOURCES["dispatch"])
 
 
-def test_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):
+def test_traffic_is_used_only_for_matching_sources_workload_and_plan(tmp_path, monkeypatch):
     path = tmp_path / "t.json"
     good = bench.kernel_source_hash(bench.OP_SOURCES["dispatch"])
-    path.write_text(json.dumps({"ops": {"dispatch": {"source_hash": good, "hbm_bytes_per_call": 5.0},
+    path.write_text(json.dumps({"workload": "k3", "plan": "waterfill",
+                                "ops": {"dispatch": {"source_hash": good, "hbm_bytes_per_call": 5.0},
                                         "combine": {"source_hash": "stale", "hbm_bytes_per_call": 6.0}}}))
     monkeypatch.setattr(bench, "TRAFFIC_PATH", str(path))
-    assert bench.traffic_for("dispatch") == 5.0
-    assert bench.traffic_for("combine") is None
+    assert bench.traffic_for("dispatch", "k3", "waterfill") == 5.0
+    assert bench.traffic_for("combine", "k3", "waterfill") is None
+    # counters taken on another workload or plan say nothing about this one
+    assert bench.traffic_for("dispatch", "decode", "waterfill") is None
+    assert bench.traffic_for("dispatch", "k3", "bounded") is None
+
+
+def test_committed_traffic_summary_names_its_workload():
+    with open(bench.TRAFFIC_PATH) as f:
+        rec = json.load(f)
+    assert rec["workload"] == "k3" and rec["plan"] == "waterfill"
+    assert "--workload" not in rec["command"] and "--plan" not in rec["command"]
 
 
 def test_algorithmic_bytes_by_hand():
