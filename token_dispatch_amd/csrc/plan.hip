@@ -58,6 +58,32 @@ static_assert(kTileEntries <= (1 << 22), "an in-tile index and an id share a wor
 static_assert(kTileEntries < (1 << 16), "a tile's count of one expert fits 16 bits");
 static_assert(kMaxE <= 1024 && (kMaxE & (kMaxE - 1)) == 0, "expert ids fit the 10-bit field of a packed placement key");
 
+// The plan kernels take a few hundred bytes of arguments (the plan's table
+// pointers). The compiler cannot hold them all in scalar registers, so it reads
+// them from the argument segment in several rounds, each waiting for its
+// scalar-cache misses before the next. Reading one word of every 64-byte line
+// of the arguments first, and waiting for them together, takes all those misses
+// in one round trip; the later reads hit the scalar cache.
+struct SolveArgs {
+    PlanShape sh;
+    PlanPtrs p;
+};
+struct TileArgs {
+    const int32_t *ids;
+    PlanShape sh;
+    PlanPtrs p;
+};
+
+template <class Args>
+__device__ __forceinline__ void touch_kernargs() {
+    constexpr int kLines = (int)((sizeof(Args) + 63) / 64);
+    const uint32_t *ka = (const uint32_t *)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t x = 0;
+#pragma unroll
+    for (int l = 0; l < kLines; ++l) x ^= ka[l * 16];
+    asm volatile("" ::"s"(x));
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS): shifts by
@@ -639,6 +665,7 @@ __device__ __forceinline__ void solve_inputs(const PlanShape &sh, const PlanPtrs
 
 __global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
+    touch_kernargs<SolveArgs>();
     int Te, st;
     solve_inputs(sh, p, Te, st);
     solve_waterfill(sh, p, smem, Te, st);
@@ -1257,6 +1284,7 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
 
 __global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
+    touch_kernargs<SolveArgs>();
     int Te, st;
     solve_inputs(sh, p, Te, st);
     solve_bounded(sh, p, smem, Te, st);
@@ -1623,6 +1651,7 @@ __device__ __forceinline__ void assign_tile(const PlanShape &sh, const PlanPtrs 
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
+    touch_kernargs<TileArgs>();
     const Tile t = tile_of(sh, blockIdx.x);
     // loads first, all in flight: the status, this wave's ids, then the tables,
     // which are only needed once the ranks are taken
@@ -1765,6 +1794,7 @@ template <bool BOUNDED>
 __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__restrict__ ids,
                                                                PlanShape sh, PlanPtrs p) {
     extern __shared__ int32_t smem[];
+    if constexpr (BOUNDED) touch_kernargs<TileArgs>();
     const int tid = threadIdx.x;
     const Tile t = tile_of(sh, blockIdx.x);
     // the tiles' status words, (water-fill) this tile's ids and the counts
