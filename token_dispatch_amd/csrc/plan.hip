@@ -38,6 +38,7 @@
 // waves of this tile) + (earlier entries of this wave), each an integer count
 // taken in entry order.
 #include <atomic>
+#include <cstddef>
 
 #include "internal.h"
 
@@ -82,6 +83,22 @@ __device__ __forceinline__ void touch_kernargs() {
 #pragma unroll
     for (int l = 0; l < kLines; ++l) x ^= ka[l * 16];
     asm volatile("" ::"s"(x));
+}
+
+// The kernel's PlanPtrs argument, read through a pointer into the argument
+// segment that the compiler cannot see through. Read as the parameter itself,
+// every pointer is loaded once at the start and held in scalar registers for the
+// whole kernel, which does not fit (the bounded fused kernel spilled 83 of them
+// to vector lanes); read this way, each is loaded from the scalar cache where it
+// is used.
+typedef __attribute__((address_space(4))) const PlanPtrs ConstPlanPtrs;
+template <class Args>
+__device__ __forceinline__ const PlanPtrs &plan_ptrs() {
+    ConstPlanPtrs *pp = (ConstPlanPtrs *)((const __attribute__((address_space(4))) char *)
+                                              __builtin_amdgcn_kernarg_segment_ptr() +
+                                          offsetof(Args, p));
+    asm volatile("" : "+s"(pp));
+    return *(const PlanPtrs *)pp;
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
@@ -663,9 +680,10 @@ __device__ __forceinline__ void solve_inputs(const PlanShape &sh, const PlanPtrs
     for (int t = tid; t < sh.n_tiles; t += kSolveThreads) st |= p.tile_status[t];
 }
 
-__global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs p) {
+__global__ __launch_bounds__(kSolveThreads) void k_solve(PlanShape sh, PlanPtrs) {
     extern __shared__ int32_t smem[];
     touch_kernargs<SolveArgs>();
+    const PlanPtrs &p = plan_ptrs<SolveArgs>();
     int Te, st;
     solve_inputs(sh, p, Te, st);
     solve_waterfill(sh, p, smem, Te, st);
@@ -1282,9 +1300,10 @@ __device__ __forceinline__ int solve_bounded(const PlanShape &sh, const PlanPtrs
     return s_status;
 }
 
-__global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs p) {
+__global__ __launch_bounds__(kSolveThreads) void k_solve_bounded(PlanShape sh, PlanPtrs) {
     extern __shared__ int32_t smem[];
     touch_kernargs<SolveArgs>();
+    const PlanPtrs &p = plan_ptrs<SolveArgs>();
     int Te, st;
     solve_inputs(sh, p, Te, st);
     solve_bounded(sh, p, smem, Te, st);
@@ -1649,9 +1668,10 @@ __device__ __forceinline__ void assign_tile(const PlanShape &sh, const PlanPtrs 
 // compiler budget scalar registers for that (the plan pointers would otherwise
 // hold enough of them to allow only one).
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs p) {
+void k_assign(const int32_t *__restrict__ ids, PlanShape sh, PlanPtrs) {
     extern __shared__ int32_t smem[];
     touch_kernargs<TileArgs>();
+    const PlanPtrs &p = plan_ptrs<TileArgs>();
     const Tile t = tile_of(sh, blockIdx.x);
     // loads first, all in flight: the status, this wave's ids, then the tables,
     // which are only needed once the ranks are taken
@@ -1791,10 +1811,9 @@ __device__ __forceinline__ void gather_counts(const PlanShape &sh, const PlanPtr
 }
 
 template <bool BOUNDED>
-__global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__restrict__ ids,
-                                                               PlanShape sh, PlanPtrs p) {
+__device__ __forceinline__ void plan_fused(const int32_t *__restrict__ ids, const PlanShape &sh,
+                                           const PlanPtrs &p) {
     extern __shared__ int32_t smem[];
-    if constexpr (BOUNDED) touch_kernargs<TileArgs>();
     const int tid = threadIdx.x;
     const Tile t = tile_of(sh, blockIdx.x);
     // the tiles' status words, (water-fill) this tile's ids and the counts
@@ -1816,6 +1835,13 @@ __global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__
     TableRegs regs = fetch_tables(sh, p, t.tile, false);
     regs.tbase = base;
     assign_tile(sh, p, t, idv, regs, sh.K >= 4 && !(status & MOONEP_STATUS_REPEAT_ID), smem);
+}
+
+template <bool BOUNDED>
+__global__ __launch_bounds__(kAssignThreads) void k_plan_fused(const int32_t *__restrict__ ids,
+                                                               PlanShape sh, PlanPtrs) {
+    touch_kernargs<TileArgs>();
+    plan_fused<BOUNDED>(ids, sh, plan_ptrs<TileArgs>());
 }
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS one workgroup may hold on gfx950
